@@ -1,0 +1,42 @@
+"""Plain fp64 CPU oracle for the joint video+text attention hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(``rope_joint_attention_amd`` and its HIP library) never calls it, and it never
+calls the product path: the two share no code.  Inputs come from ``hvinputs``,
+which holds no arithmetic of the method.
+
+Each function restates, in NumPy float64, what the HunyuanVideo notes page
+("HunyuanVideo 模型结构与数学原理", note.shouss.top) says is computed:
+
+* ``token_grid``      section 4 (Causal 3D VAE) latent-size and token-count formulas;
+* ``apply_rope3d``    section 5.5 (3D RoPE), a direct sum of three 1-D rotary
+                      embeddings over channel blocks (16, 56, 56);
+* ``joint_attention`` section 5.2 (double-stream block) joint softmax attention
+                      over the video-then-text sequence, scale 1/sqrt(128),
+                      with padded text keys left out (section 3.1 keeps at
+                      most 256 prompt tokens; section 5.2 names the valid
+                      text length);
+* ``hot_path``        the three in sequence.
+
+Nothing here is blocked, fused or reordered beyond the formulas: the matrix
+products use NumPy's matmul as a library primitive, and query rows are
+processed in independent chunks only to bound memory.
+
+Pins (tests/test_oracle_*.py): printed token counts, closed-form rotation
+angles, norm and relative-position invariants, the complex-number form of
+RoPE, uniform/one-key/two-key closed forms, permutation and shift
+invariance, masking with poisoned values, and a pure-Python brute force.
+"""
+from .hv_oracle import (  # noqa: F401
+    HEADS,
+    HEAD_DIM,
+    ROPE_AXES,
+    OracleGrid,
+    token_grid,
+    rope_frequencies,
+    video_coordinates,
+    apply_rope3d,
+    joint_attention,
+    hot_path,
+)

@@ -1,0 +1,182 @@
+"""fp64 reference implementation (test infrastructure; see package docstring).
+
+Citations name the HunyuanVideo notes page ("HunyuanVideo 模型结构与数学原理",
+note.shouss.top, page 1 of the source set) and the summary page of the
+technical report (zhao9797.github.io, "hunyuan-video"), by section.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+HEADS = 24       # notes page, section 5.1: hidden 3072 = 24 heads x 128
+HEAD_DIM = 128
+
+# Notes page section 5.5 / report summary Table 2: per-head channels split
+# (d_t, d_h, d_w) = (16, 56, 56) in that order.  (axis, first channel, width)
+ROPE_AXES = (("t", 0, 16), ("h", 16, 56), ("w", 72, 56))
+
+
+@dataclasses.dataclass(frozen=True)
+class OracleGrid:
+    frames: int
+    height: int
+    width: int
+    t_lat: int   # T'
+    h_lat: int   # H' = H / 8
+    w_lat: int   # W' = W / 8
+    gt: int      # token grid along time   = T'
+    gh: int      # token grid along height = H' / 2
+    gw: int      # token grid along width  = W' / 2
+    n_video: int
+
+
+def token_grid(frames: int, height: int, width: int) -> OracleGrid:
+    """Latent and token grid of an F x H x W clip.
+
+    Notes page section 4: the causal VAE compresses time by 4 and space by 8,
+    valid for F = 4k + 1, giving T' = floor((F - 1) / 4) + 1, H' = H / 8,
+    W' = W / 8; the 1x2x2 patch embedding then gives
+    N = T' * (H' / 2) * (W' / 2).  Section 8 checks that the frame size is a
+    multiple of 16 and the frame count is 4k + 1 before running.
+    """
+    for name, val in (("frames", frames), ("height", height), ("width", width)):
+        if not isinstance(val, (int, np.integer)) or val <= 0:
+            raise ValueError(f"{name} must be a positive integer, got {val!r}")
+    if (frames - 1) % 4 != 0:
+        raise ValueError(f"frames must be 4k+1, got {frames}")
+    if height % 16 != 0 or width % 16 != 0:
+        raise ValueError(f"height and width must be multiples of 16, got {height}x{width}")
+    t_lat = (frames - 1) // 4 + 1
+    h_lat = height // 8
+    w_lat = width // 8
+    gt, gh, gw = t_lat, h_lat // 2, w_lat // 2
+    return OracleGrid(frames, height, width, t_lat, h_lat, w_lat, gt, gh, gw, gt * gh * gw)
+
+
+def rope_frequencies(theta: float):
+    """Per-axis rotation frequencies theta^(-2j/d_a), j < d_a/2.
+
+    Section 5.5 writes R_3D as the direct sum R_t + R_h + R_w of one-dimensional
+    rotary embeddings (RoFormer); each axis block uses the RoFormer frequencies
+    over its own width d_a.  Returned as {axis: float64 array}.
+    """
+    out = {}
+    for axis, _off, d in ROPE_AXES:
+        j = np.arange(d // 2, dtype=np.float64)
+        out[axis] = np.power(np.float64(theta), -2.0 * j / d)
+    return out
+
+
+def video_coordinates(grid: OracleGrid) -> np.ndarray:
+    """Integer (t, h, w) patch coordinates of every video token, shape [N, 3].
+
+    The patchified latent is flattened t-major then row-major (a meshgrid
+    over the T' x H'/2 x W'/2 grid), coordinates start at 0 with unit step.
+    """
+    t, h, w = np.meshgrid(np.arange(grid.gt), np.arange(grid.gh), np.arange(grid.gw),
+                          indexing="ij")
+    return np.stack([t.reshape(-1), h.reshape(-1), w.reshape(-1)], axis=1).astype(np.int64)
+
+
+def apply_rope3d(x: np.ndarray, token_index: np.ndarray, grid: OracleGrid,
+                 theta: float) -> np.ndarray:
+    """Rotate the rows of ``x`` that are video tokens; return a float64 copy.
+
+    ``x``: float64 [..., R, HEADS, HEAD_DIM]; ``token_index``: [R] sequence
+    position of each row.  Rows with position >= N (text) are returned
+    unchanged.  For a video token with coordinates (t, h, w), every head's
+    channel pair (o_a + 2j, o_a + 2j + 1) of axis block a is rotated by the
+    angle pos_a * theta^(-2j/d_a):
+        x0' = x0 cos(phi) - x1 sin(phi),  x1' = x0 sin(phi) + x1 cos(phi).
+    Only Q and K are passed through here; V is never rotated (section 5.5:
+    RoPE is applied to the visual Q, K only).
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    token_index = np.asarray(token_index, dtype=np.int64)
+    assert x.shape[-3] == token_index.shape[0] and x.shape[-1] == HEAD_DIM
+    coords = video_coordinates(grid)
+    freqs = rope_frequencies(theta)
+    video_rows = np.nonzero(token_index < grid.n_video)[0]
+    chunk = 4096
+    for s in range(0, video_rows.size, chunk):
+        rows = video_rows[s:s + chunk]
+        pos = coords[token_index[rows]]                  # [r, 3]
+        for a, (axis, off, d) in enumerate(ROPE_AXES):
+            phi = pos[:, a:a + 1].astype(np.float64) * freqs[axis][None, :]   # [r, d/2]
+            c = np.cos(phi)[:, None, :]                  # broadcast over heads
+            sn = np.sin(phi)[:, None, :]
+            sel = x[..., rows, :, off:off + d]
+            x0 = sel[..., 0::2].copy()
+            x1 = sel[..., 1::2].copy()
+            sel[..., 0::2] = x0 * c - x1 * sn
+            sel[..., 1::2] = x0 * sn + x1 * c
+            x[..., rows, :, off:off + d] = sel
+    return x
+
+
+def joint_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_video: int,
+                    valid: Sequence[int], scale: Optional[float] = None,
+                    rows: Optional[np.ndarray] = None,
+                    heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Exact joint softmax attention, float64.
+
+    Section 5.2: Q = [Q_v; Q_t], K = [K_v; K_t], V = [V_v; V_t] along the
+    sequence (video first) and Attn = softmax(Q K^T / sqrt(128)) V per head.
+    Text keys at positions >= n_video + valid[b] are padding and are excluded
+    from the softmax.  Every query row (padded text rows included) attends to
+    the same valid keys.
+
+    ``q``: float64 [B, Rq, H, D] holding the query rows listed in ``rows``
+    (all L rows when ``rows`` is None); ``k``, ``v``: float64 [B, L, H, D].
+    Returns float64 [B, Rq, H', D] for the heads listed in ``heads``.
+    """
+    B, L, H, D = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if heads is None:
+        heads = range(H)
+    heads = list(heads)
+    Rq = q.shape[1]
+    out = np.zeros((B, Rq, len(heads), D), dtype=np.float64)
+    for b in range(B):
+        lk = n_video + int(valid[b])
+        if lk <= 0:
+            raise ValueError("no valid keys")
+        for hi, h in enumerate(heads):
+            kb = np.ascontiguousarray(k[b, :lk, h, :])
+            vb = np.ascontiguousarray(v[b, :lk, h, :])
+            for s in range(0, Rq, 256):
+                qb = q[b, s:s + 256, h, :]
+                scores = (qb @ kb.T) * scale
+                m = scores.max(axis=1, keepdims=True)
+                p = np.exp(scores - m)
+                z = p.sum(axis=1, keepdims=True)
+                out[b, s:s + 256, hi, :] = (p @ vb) / z
+    return out
+
+
+def hot_path(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
+             frames: int, height: int, width: int, valid: Sequence[int],
+             theta: float, rows: Optional[np.ndarray] = None,
+             heads: Optional[Sequence[int]] = None, scale: Optional[float] = None):
+    """Token grid -> 3D RoPE on video Q, K -> joint attention, all float64.
+
+    ``*_bits``: bfloat16 bit patterns [B, L, H, D] (uint16), widened exactly.
+    Returns (grid, out) with out float64 [B, len(rows), H', D].
+    """
+    from hvinputs import bf16_bits_to_f64  # storage decoding only
+
+    grid = token_grid(frames, height, width)
+    B, L = k_bits.shape[:2]
+    if rows is None:
+        rows = np.arange(L)
+    rows = np.asarray(rows, dtype=np.int64)
+    qf = apply_rope3d(bf16_bits_to_f64(q_bits[:, rows]), rows, grid, theta)
+    kf = apply_rope3d(bf16_bits_to_f64(k_bits), np.arange(L), grid, theta)
+    vf = bf16_bits_to_f64(v_bits)
+    out = joint_attention(qf, kf, vf, grid.n_video, valid, scale=scale, heads=heads)
+    return grid, out
