@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the joint video+text attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one synthetic batch:
+hv_token_grid -> hv_rope3d_apply (video Q/K, in place) -> hv_joint_attention_fwd.
+Inputs are generated on the host, copied to HBM before timing, and stay
+resident.  RoPE works in place, so step i rotates the output of step i-1: the
+same bytes and arithmetic as a fresh batch.
+
+Printed: ONE JSON line (stdout) with the whole-step throughput in attention
+TFLOP/s (algorithmic FLOPs 4*heads*head_dim*sum_b L*Lk_b over the step time),
+per-kernel times from HIP events on the launch stream, the attention
+kernel's MFMA roofline fraction, and the fp64 oracle timed on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "joint-attn TFLOP/s, ms/call and % MFMA peak at 720×1280×129 (L=119056)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+HEADS, HEAD_DIM = 24, 128
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_flops(batch: int, seq_len: int, lk) -> float:
+    return 4.0 * HEADS * HEAD_DIM * sum(float(seq_len) * x for x in lk)
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "rope_joint_attention_amd", "csrc", "attn_fwd.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not b or h.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(bits, wl, n_video, seq_len, rows_n: int):
+    """The fp64 oracle (unchanged) on a bounded sample: rows_n query rows of every
+    head and batch entry, against all keys, including its RoPE of all of K."""
+    import numpy as np
+
+    from oracle import hot_path
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    rows = np.sort(rng.choice(seq_len, size=rows_n, replace=False))
+    t0 = time.perf_counter()
+    hot_path(bits["q"], bits["k"], bits["v"], wl.frames, wl.height, wl.width, wl.valid, wl.theta,
+             rows=rows)
+    dt = time.perf_counter() - t0
+    lk = [n_video + v for v in wl.valid]
+    flops = 4.0 * HEADS * HEAD_DIM * rows_n * sum(lk)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{rows_n} random query rows x {HEADS} heads x batch {wl.batch} against all "
+                   f"{max(lk)} keys of {wl.name}, incl. fp64 RoPE of all K; {dt:.1f} s"),
+        "seconds": dt,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the hot path is built and timed on a single "
+              "MI355X (no sharding or collectives in this library); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import hvinputs
+    import rope_joint_attention_amd as hv
+
+    hv.load_library()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    name = args.workload or hvinputs.HEADLINE
+    wl = hvinputs.WORKLOADS[name]
+    grid = hv.hv_token_grid(wl.frames, wl.height, wl.width)
+    L = grid.n_video + wl.text_capacity
+    lk = [grid.n_video + v for v in wl.valid]
+    progress(f"workload {name}: B={wl.batch} L={L} N={grid.n_video} valid={list(wl.valid)}")
+
+    t0 = time.perf_counter()
+    bits = hvinputs.draw_qkv(wl.batch, L, wl.seed)
+    progress(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
+
+    def to_dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(bits["q"]), to_dev(bits["k"]), to_dev(bits["v"])
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        g = hv.hv_token_grid(wl.frames, wl.height, wl.width)
+        if ev is not None:
+            ev[0].record(stream)
+        hv.hv_rope3d_apply(q, k, g, wl.theta)
+        if ev is not None:
+            ev[1].record(stream)
+        hv.hv_joint_attention_fwd(q, k, v, list(wl.valid), g.n_video, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    progress(f"warmup {args.warmup} done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rope_ms = [e[0].elapsed_time(e[1]) for e in events]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in events]
+    progress(f"timed {args.steps} steps in {wall:.2f} s")
+
+    if args.copy_ref_mib > 0:
+        n = args.copy_ref_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        progress(f"reference copy of {args.copy_ref_mib} MiB done (x3)")
+
+    flops = attn_flops(wl.batch, L, lk)
+    ms_step = wall * 1000.0 / args.steps
+    attn_avg = float(np.mean(attn_ms))
+    rope_avg = float(np.mean(rope_ms))
+    achieved = flops / (attn_avg / 1000.0) / 1e12
+    rope_bytes = 4.0 * wl.batch * grid.n_video * HEADS * HEAD_DIM * 2
+    rope_gbps = rope_bytes / (rope_avg / 1000.0) / 1e9
+    traffic = recorded_traffic(name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step / 1000.0) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": wl.batch, "seq_len": L, "n_video": grid.n_video,
+                   "text_valid": list(wl.valid), "heads": HEADS, "head_dim": HEAD_DIM,
+                   "theta": wl.theta, "frames_hw": [wl.frames, wl.height, wl.width]},
+        "attn_ms_per_call": round(attn_avg, 4),
+        "attn_ms_min": round(float(np.min(attn_ms)), 4),
+        "attn_tflops": round(achieved, 2),
+        "pct_mfma_peak": round(100.0 * achieved / PEAK_BF16_TFLOPS, 2),
+        "rope_ms_per_call": round(rope_avg, 4),
+        "rope_GBps": round(rope_gbps, 1),
+        "rope_pct_hbm_peak": round(100.0 * rope_gbps / PEAK_HBM_GBPS, 2),
+        "attn_flops_per_call": flops,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        progress("timing the fp64 oracle on a bounded sample (host cores)")
+        cb = cpu_baseline(bits, wl, grid.n_video, L, args.cpu_rows)
+        cb.pop("seconds", None)
+        cb["value"] = round(cb["value"], 6)
+        result["cpu_baseline"] = cb
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

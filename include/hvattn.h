@@ -1,0 +1,136 @@
+/*
+ * hvattn.h -- C ABI of libhvattn: the joint video+text attention hot path of a
+ * HunyuanVideo-style diffusion transformer, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what is computed (all on the HunyuanVideo notes page
+ * "HunyuanVideo 模型结构与数学原理", note.shouss.top, unless stated):
+ *   - token grid: section 4 (Causal 3D VAE latent size, 1x2x2 patch count);
+ *   - 3D RoPE:    section 5.5 (R_3D = R_t (+) R_h (+) R_w, channel split
+ *                 (16, 56, 56)); the technical-report summary page
+ *                 (zhao9797.github.io, "hunyuan-video"), Table 2 paragraph,
+ *                 gives the same split;
+ *   - attention:  section 5.2 (joint softmax attention over [video; text],
+ *                 scale 1/sqrt(128)); section 3.1 (at most 256 text tokens);
+ *                 section 5.1 (24 heads x 128).
+ *
+ * Conventions shared by all calls
+ *   - Tensors are bfloat16 bit patterns (hv_bf16) in device memory owned by
+ *     the caller, laid out [batch][seq][head][channel] with the channel dim
+ *     contiguous, head stride 128 elements, token stride layout->stride_l
+ *     and batch stride layout->stride_b (both in elements).  The sequence
+ *     holds the n_video video tokens first, then the text tokens.
+ *   - Device pointers must be 16-byte aligned; strides must be multiples of
+ *     8 elements, stride_l >= heads*head_dim, stride_b >= seq_len*stride_l.
+ *   - heads must be 24 and head_dim 128, batch <= HV_MAX_BATCH and
+ *     seq_len <= HV_MAX_SEQ (HV_ERR_UNSUPPORTED otherwise); negative sizes
+ *     are HV_ERR_INVALID_ARG.  A call with batch == 0 or seq_len == 0 has
+ *     nothing to do and returns HV_OK without launching (so does RoPE with
+ *     n_video == 0).
+ *   - Every argument is validated on the host before any HIP call; an
+ *     invalid call returns a negative status and touches no memory.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without synchronising.  Faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - The library allocates no memory and keeps no mutable global state;
+ *     calls are thread-safe.  Calls that write overlapping memory on
+ *     different streams race, as with any kernel.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef HVATTN_H
+#define HVATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HV_HEADS 24
+#define HV_HEAD_DIM 128
+#define HV_MAX_BATCH 64
+#define HV_MAX_SEQ (1 << 24)
+
+typedef uint16_t hv_bf16; /* raw bfloat16 bits */
+
+enum hv_status {
+  HV_OK = 0,
+  HV_ERR_INVALID_ARG = -1, /* NULL, bad size, range, alignment or overlap */
+  HV_ERR_UNSUPPORTED = -2, /* heads != 24, head_dim != 128, batch/seq too large */
+  HV_ERR_HIP = -3          /* a HIP launch failed (e.g. no device) */
+};
+
+/* Latent and token grid of a clip (notes page, section 4).
+ *   t_lat = floor((frames-1)/4) + 1, h_lat = height/8, w_lat = width/8
+ *   gt = t_lat, gh = h_lat/2, gw = w_lat/2   (1x2x2 patches)
+ *   n_video = gt*gh*gw                        (video tokens) */
+typedef struct hv_grid {
+  int32_t frames, height, width;
+  int32_t t_lat, h_lat, w_lat;
+  int32_t gt, gh, gw;
+  int32_t reserved; /* 0 */
+  int64_t n_video;
+} hv_grid;
+
+typedef struct hv_layout {
+  int32_t batch;    /* B */
+  int32_t seq_len;  /* L = n_video + text capacity */
+  int32_t heads;    /* must be HV_HEADS */
+  int32_t head_dim; /* must be HV_HEAD_DIM */
+  int64_t stride_b; /* elements between batch entries */
+  int64_t stride_l; /* elements between consecutive tokens */
+} hv_layout;
+
+/* hv_token_grid: fill *out for an F x H x W clip (host only, no GPU use).
+ * Notes page section 4 gives the formula for F = 4k+1; section 8 states that
+ * sizes must be multiples of 16 and frames 4k+1 to pass the input check.
+ * Errors: HV_ERR_INVALID_ARG if out is NULL, any size <= 0, frames != 4k+1,
+ * or height/width not multiples of 16.  *out is untouched on error. */
+int hv_token_grid(int32_t frames, int32_t height, int32_t width, hv_grid* out);
+
+/* hv_rope3d_apply: rotate the video rows of q and k in place (notes page
+ * section 5.5).  For every batch entry b, video token n < grid->n_video with
+ * patch coordinates t = n / (gh*gw), h = (n / gw) % gh, w = n % gw, and every
+ * head, the channel pair (o + 2j, o + 2j + 1) of axis block
+ * (o, d) in {(0,16) for t, (16,56) for h, (72,56) for w} is rotated by
+ * angle pos * theta^(-2j/d):  x0' = x0 cos - x1 sin,  x1' = x0 sin + x1 cos.
+ * Rotation math is fp32, results are rounded to bf16 (nearest even).
+ * Text rows (n >= n_video) and V are never touched.
+ *   q, k    device pointers, layout *layout; may not overlap each other
+ *   grid    from hv_token_grid; layout->seq_len >= grid->n_video
+ *   theta   rotary base, finite and > 0 (10000 in the benchmark workloads)
+ * Errors: HV_ERR_INVALID_ARG (NULL, inconsistent grid, theta <= 0,
+ * alignment, overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+int hv_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
+                    const hv_grid* grid, float theta, void* stream);
+
+/* hv_joint_attention_fwd: out = softmax(scale * Q K^T) V per (batch, head)
+ * over the joint [video; text] sequence (notes page section 5.2).
+ * Keys at positions >= n_video + text_valid_len[b] are padding and take no
+ * part in the softmax; every one of the seq_len query rows (padded text rows
+ * included) attends to the same valid keys.  bf16 inputs, fp32 accumulation
+ * and softmax, output rounded to bf16 (nearest even).
+ *   q, k, v         device pointers, layout *layout (q, k already rotated)
+ *   text_valid_len  HOST array of layout->batch int32 values in
+ *                   [0, seq_len - n_video]; NULL means all text is valid
+ *   out             device pointer, same layout; must not overlap q, k, v
+ *   n_video         video tokens at the head of the sequence, 0..seq_len
+ *   softmax_scale   > 0 to override; <= 0 or NaN selects 1/sqrt(128)
+ * n_video + text_valid_len[b] must be >= 1 for every b.  batch == 0 or
+ * seq_len == 0 is an empty call and returns HV_OK without launching.
+ * Errors: HV_ERR_INVALID_ARG, HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                           const int32_t* text_valid_len, hv_bf16* out,
+                           const hv_layout* layout, int64_t n_video,
+                           float softmax_scale, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* hv_status_string(int status);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int hv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HVATTN_H */

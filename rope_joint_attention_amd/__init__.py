@@ -1,0 +1,184 @@
+"""rope_joint_attention_amd: Python binding of libhvattn (MI355X / gfx950).
+
+A thin ctypes layer over the C ABI in include/hvattn.h.  The functions keep
+the C names and only marshal arguments: torch tensors become device pointers
+and strides, the current torch stream becomes the HIP stream.  Every step of
+the computation runs in the HIP kernels of libhvattn.so; if the library is
+not built, every call raises (there is no fallback).
+
+    hv_token_grid(frames, height, width) -> HvGrid
+    hv_rope3d_apply(q, k, grid, theta)          # in place on video rows
+    hv_joint_attention_fwd(q, k, v, text_valid_len, n_video, out=None,
+                           softmax_scale=None) -> out
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "HV_HEADS", "HV_HEAD_DIM", "HV_MAX_BATCH", "HvError", "HvGrid",
+    "hv_token_grid", "hv_rope3d_apply", "hv_joint_attention_fwd",
+    "hv_status_string", "library_path", "load_library",
+]
+
+HV_HEADS = 24
+HV_HEAD_DIM = 128
+HV_MAX_BATCH = 64
+HV_OK, HV_ERR_INVALID_ARG, HV_ERR_UNSUPPORTED, HV_ERR_HIP = 0, -1, -2, -3
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "lib", "libhvattn.so")
+
+
+class HvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {hv_status_string(status)} (status {status})")
+
+
+class _Grid(ctypes.Structure):
+    _fields_ = [("frames", ctypes.c_int32), ("height", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("t_lat", ctypes.c_int32), ("h_lat", ctypes.c_int32), ("w_lat", ctypes.c_int32),
+                ("gt", ctypes.c_int32), ("gh", ctypes.c_int32), ("gw", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("n_video", ctypes.c_int64)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("stride_b", ctypes.c_int64), ("stride_l", ctypes.c_int64)]
+
+
+class HvGrid:
+    """Result of hv_token_grid (mirrors struct hv_grid)."""
+
+    __slots__ = ("frames", "height", "width", "t_lat", "h_lat", "w_lat", "gt", "gh", "gw", "n_video")
+
+    def __init__(self, g: _Grid):
+        for name in self.__slots__:
+            setattr(self, name, int(getattr(g, name)))
+
+    def _c(self) -> _Grid:
+        g = _Grid()
+        for name in self.__slots__:
+            setattr(g, name, getattr(self, name))
+        return g
+
+    def __repr__(self):
+        return ("HvGrid(" + ", ".join(f"{n}={getattr(self, n)}" for n in self.__slots__) + ")")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libhvattn.so from the package directory (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libhvattn.so is not built ({path}); run "
+                           f"`python -m rope_joint_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.hv_token_grid.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Grid)]
+    lib.hv_token_grid.restype = ctypes.c_int
+    lib.hv_rope3d_apply.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Layout),
+                                    ctypes.POINTER(_Grid), ctypes.c_float, ctypes.c_void_p]
+    lib.hv_rope3d_apply.restype = ctypes.c_int
+    lib.hv_joint_attention_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p,
+                                           ctypes.POINTER(_Layout), ctypes.c_int64, ctypes.c_float,
+                                           ctypes.c_void_p]
+    lib.hv_joint_attention_fwd.restype = ctypes.c_int
+    lib.hv_status_string.argtypes = [ctypes.c_int]
+    lib.hv_status_string.restype = ctypes.c_char_p
+    lib.hv_version.argtypes = []
+    lib.hv_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def hv_status_string(status: int) -> str:
+    return load_library().hv_status_string(int(status)).decode()
+
+
+def hv_token_grid(frames: int, height: int, width: int) -> HvGrid:
+    g = _Grid()
+    st = load_library().hv_token_grid(int(frames), int(height), int(width), ctypes.byref(g))
+    if st != HV_OK:
+        raise HvError(st, f"hv_token_grid({frames}, {height}, {width})")
+    return HvGrid(g)
+
+
+def _layout_of(t, what: str) -> _Layout:
+    import torch
+
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{what} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{what} must be a GPU tensor")
+    if t.dim() != 4 or t.shape[2] != HV_HEADS or t.shape[3] != HV_HEAD_DIM:
+        raise ValueError(f"{what} must be [batch, seq, {HV_HEADS}, {HV_HEAD_DIM}], got {tuple(t.shape)}")
+    if t.stride(3) != 1 or t.stride(2) != HV_HEAD_DIM:
+        raise ValueError(f"{what} needs contiguous heads x channels, strides {t.stride()}")
+    lay = _Layout()
+    lay.batch, lay.seq_len = t.shape[0], t.shape[1]
+    lay.heads, lay.head_dim = HV_HEADS, HV_HEAD_DIM
+    lay.stride_b, lay.stride_l = t.stride(0), t.stride(1)
+    return lay
+
+
+def _same_layout(a: _Layout, b: _Layout) -> bool:
+    return all(getattr(a, f) == getattr(b, f) for f, _ in _Layout._fields_)
+
+
+def _stream_of(t):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def hv_rope3d_apply(q, k, grid: HvGrid, theta: float = 10000.0) -> None:
+    """Rotate the video rows of q and k in place (see hvattn.h)."""
+    lay = _layout_of(q, "q")
+    if not _same_layout(lay, _layout_of(k, "k")):
+        raise ValueError("q and k must share shape and strides")
+    g = grid._c()
+    st = load_library().hv_rope3d_apply(q.data_ptr(), k.data_ptr(), ctypes.byref(lay),
+                                        ctypes.byref(g), float(theta), _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_rope3d_apply")
+
+
+def hv_joint_attention_fwd(q, k, v, text_valid_len: Optional[Sequence[int]], n_video: int,
+                           out=None, softmax_scale: Optional[float] = None):
+    """Joint [video; text] attention forward (see hvattn.h); returns out."""
+    import torch
+
+    lay = _layout_of(q, "q")
+    for t, name in ((k, "k"), (v, "v")):
+        if not _same_layout(lay, _layout_of(t, name)):
+            raise ValueError(f"q and {name} must share shape and strides")
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    elif not _same_layout(lay, _layout_of(out, "out")):
+        raise ValueError("out must share shape and strides with q")
+    valid_arr = None
+    if text_valid_len is not None:
+        vals = [int(x) for x in text_valid_len]
+        if len(vals) != q.shape[0]:
+            raise ValueError("text_valid_len needs one entry per batch element")
+        valid_arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = load_library().hv_joint_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), valid_arr,
+                                               out.data_ptr(), ctypes.byref(lay), int(n_video),
+                                               scale, _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_joint_attention_fwd")
+    return out

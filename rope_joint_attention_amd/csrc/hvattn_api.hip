@@ -1,0 +1,158 @@
+// C ABI of libhvattn: argument validation, launch geometry, status codes.
+// Every check runs on the host before the first HIP call, so each error path
+// can be exercised without a GPU.
+#include <math.h>
+#include <string.h>
+
+#include "hv_internal.h"
+
+namespace {
+
+constexpr int64_t kRowElems = (int64_t)HV_HEADS * HV_HEAD_DIM;  // 3072
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Validate a layout; on success *extent is the number of elements a tensor
+// spans from its base pointer.
+int check_layout(const hv_layout* lay, int64_t* extent) {
+  if (!lay) return HV_ERR_INVALID_ARG;
+  if (lay->batch < 0 || lay->seq_len < 0 || lay->heads <= 0 || lay->head_dim <= 0)
+    return HV_ERR_INVALID_ARG;
+  if (lay->heads != HV_HEADS || lay->head_dim != HV_HEAD_DIM) return HV_ERR_UNSUPPORTED;
+  if (lay->batch > HV_MAX_BATCH || lay->seq_len > HV_MAX_SEQ) return HV_ERR_UNSUPPORTED;
+  if (lay->stride_l < kRowElems || (lay->stride_l & 7) != 0) return HV_ERR_INVALID_ARG;
+  if ((lay->stride_b & 7) != 0) return HV_ERR_INVALID_ARG;
+  if (lay->batch > 1 && lay->stride_b < (int64_t)lay->seq_len * lay->stride_l)
+    return HV_ERR_INVALID_ARG;
+  if (lay->batch == 0 || lay->seq_len == 0) {
+    *extent = 0;
+  } else {
+    *extent = (int64_t)(lay->batch - 1) * lay->stride_b +
+              (int64_t)(lay->seq_len - 1) * lay->stride_l + kRowElems;
+  }
+  return HV_OK;
+}
+
+bool overlap(const void* a, const void* b, int64_t elems) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  const uintptr_t n = (uintptr_t)elems * sizeof(hv_bf16);
+  return x < y + n && y < x + n;
+}
+
+int check_grid(const hv_grid* g) {
+  if (!g) return HV_ERR_INVALID_ARG;
+  if (g->gt <= 0 || g->gh <= 0 || g->gw <= 0) return HV_ERR_INVALID_ARG;
+  if (g->n_video != (int64_t)g->gt * g->gh * g->gw) return HV_ERR_INVALID_ARG;
+  return HV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hv_version(void) { return 10000; }
+
+const char* hv_status_string(int status) {
+  switch (status) {
+    case HV_OK: return "HV_OK: success";
+    case HV_ERR_INVALID_ARG: return "HV_ERR_INVALID_ARG: invalid argument (NULL, size, range, alignment or overlap)";
+    case HV_ERR_UNSUPPORTED: return "HV_ERR_UNSUPPORTED: unsupported shape (heads must be 24, head_dim 128, batch/seq within limits)";
+    case HV_ERR_HIP: return "HV_ERR_HIP: HIP launch failed";
+    default: return "unknown hv status";
+  }
+}
+
+int hv_token_grid(int32_t frames, int32_t height, int32_t width, hv_grid* out) {
+  if (!out) return HV_ERR_INVALID_ARG;
+  if (frames <= 0 || height <= 0 || width <= 0) return HV_ERR_INVALID_ARG;
+  if ((frames - 1) % 4 != 0) return HV_ERR_INVALID_ARG;
+  if (height % 16 != 0 || width % 16 != 0) return HV_ERR_INVALID_ARG;
+  hv_grid g;
+  memset(&g, 0, sizeof(g));
+  g.frames = frames;
+  g.height = height;
+  g.width = width;
+  g.t_lat = (frames - 1) / 4 + 1;  // causal VAE keeps the first frame, then 4x in time
+  g.h_lat = height / 8;            // 8x in space
+  g.w_lat = width / 8;
+  g.gt = g.t_lat;                  // 1x2x2 patches
+  g.gh = g.h_lat / 2;
+  g.gw = g.w_lat / 2;
+  g.n_video = (int64_t)g.gt * g.gh * g.gw;
+  *out = g;
+  return HV_OK;
+}
+
+int hv_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout, const hv_grid* grid,
+                    float theta, void* stream) {
+  int64_t extent = 0;
+  int st = check_layout(layout, &extent);
+  if (st != HV_OK) return st;
+  st = check_grid(grid);
+  if (st != HV_OK) return st;
+  if (!(theta > 0.f) || !isfinite(theta)) return HV_ERR_INVALID_ARG;
+  if (grid->n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
+  if (!q || !k) return HV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k)) return HV_ERR_INVALID_ARG;
+  if (overlap(q, k, extent)) return HV_ERR_INVALID_ARG;
+  if (layout->batch == 0 || layout->seq_len == 0 || grid->n_video == 0) return HV_OK;
+
+  hv::RopeParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.stride_b = layout->stride_b;
+  p.stride_l = layout->stride_l;
+  p.batch = layout->batch;
+  p.n_video = (int32_t)grid->n_video;
+  p.gh = grid->gh;
+  p.gw = grid->gw;
+  // (offset, width) of the time, height and width blocks: (0,16), (16,56), (72,56)
+  const int widths[3] = {16, 56, 56};
+  int pair = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < widths[a] / 2; ++j)
+      p.freq[pair++] = (float)pow((double)theta, -2.0 * j / widths[a]);
+  const hipError_t e = hv::launch_rope3d(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
+int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                           const int32_t* text_valid_len, hv_bf16* out,
+                           const hv_layout* layout, int64_t n_video, float softmax_scale,
+                           void* stream) {
+  int64_t extent = 0;
+  int st = check_layout(layout, &extent);
+  if (st != HV_OK) return st;
+  if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out) return HV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HV_ERR_INVALID_ARG;
+  if (overlap(out, q, extent) || overlap(out, k, extent) || overlap(out, v, extent))
+    return HV_ERR_INVALID_ARG;
+  if (layout->batch == 0 || layout->seq_len == 0) return HV_OK;
+
+  hv::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  const int64_t text_cap = layout->seq_len - n_video;
+  for (int b = 0; b < layout->batch; ++b) {
+    const int64_t valid = text_valid_len ? text_valid_len[b] : text_cap;
+    if (valid < 0 || valid > text_cap) return HV_ERR_INVALID_ARG;
+    if (n_video + valid < 1) return HV_ERR_INVALID_ARG;
+    p.lk[b] = (int32_t)(n_video + valid);
+  }
+  float scale = softmax_scale;
+  if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf((float)HV_HEAD_DIM);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.stride_b = layout->stride_b;
+  p.stride_l = layout->stride_l;
+  p.batch = layout->batch;
+  p.seq_len = layout->seq_len;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
+  const hipError_t e = hv::launch_attn_fwd(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
+}  // extern "C"

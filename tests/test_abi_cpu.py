@@ -1,0 +1,180 @@
+"""C-ABI checks that need no GPU.
+
+* libhvattn.so loads and exports every function include/hvattn.h declares;
+* hv_token_grid (host-only) agrees with the printed values and the oracle;
+* every host-side validation path of hv_rope3d_apply and
+  hv_joint_attention_fwd returns its documented status without touching
+  memory (fake, never-dereferenced device addresses are passed; the
+  library validates everything before its first HIP call).
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import rope_joint_attention_amd as hv
+from oracle import token_grid as oracle_grid
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hvattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hv.library_path()),
+                                reason="libhvattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = hv.load_library()
+    names = declared_functions()
+    assert set(names) >= {"hv_token_grid", "hv_rope3d_apply", "hv_joint_attention_fwd",
+                          "hv_status_string", "hv_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    # and nothing else hv_* is exported that the header does not declare
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", hv.library_path()], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r" T (hv_[a-z0-9_]+)$", out, flags=re.M)))
+    assert exported == names
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, 7):
+        s = hv.hv_status_string(st)
+        assert isinstance(s, str) and s
+    assert "INVALID" in hv.hv_status_string(-1)
+    assert hv.load_library().hv_version() >= 10000
+
+
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "token_grid.json")))
+
+
+def test_token_grid_printed_values():
+    for c in GOLDEN["cases"]:
+        g = hv.hv_token_grid(c["frames"], c["height"], c["width"])
+        if "n_video" in c:
+            assert g.n_video == c["n_video"]
+        if "latent" in c:
+            assert (g.t_lat, g.h_lat, g.w_lat) == tuple(c["latent"])
+        if "token_grid" in c:
+            assert (g.gt, g.gh, g.gw) == tuple(c["token_grid"])
+
+
+@pytest.mark.parametrize("fhw", [(f, h, w) for f in (1, 5, 17, 33, 65, 129, 257)
+                                 for h, w in ((256, 256), (544, 960), (720, 1280), (1104, 832), (16, 16), (960, 960))])
+def test_token_grid_matches_oracle(fhw):
+    g = hv.hv_token_grid(*fhw)
+    o = oracle_grid(*fhw)
+    for f in ("t_lat", "h_lat", "w_lat", "gt", "gh", "gw", "n_video"):
+        assert getattr(g, f) == getattr(o, f), f
+
+
+@pytest.mark.parametrize("fhw", GOLDEN["rejected"]["cases"] + [[-3, 544, 960], [17, 544, -16], [2, 16, 16]])
+def test_token_grid_rejects(fhw):
+    with pytest.raises(hv.HvError) as ei:
+        hv.hv_token_grid(*fhw)
+    assert ei.value.status == hv.HV_ERR_INVALID_ARG
+
+
+def test_token_grid_null_out():
+    lib = hv.load_library()
+    assert lib.hv_token_grid(17, 544, 960, None) == hv.HV_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- validation
+FAKE = 1 << 40           # 16-byte aligned, never dereferenced
+SEP = 1 << 34            # far apart so default tensors never overlap
+
+
+def layout(batch=1, seq=300, heads=24, dim=128, sb=None, sl=3072):
+    lay = hv._Layout()
+    lay.batch, lay.seq_len, lay.heads, lay.head_dim = batch, seq, heads, dim
+    lay.stride_l = sl
+    lay.stride_b = seq * sl if sb is None else sb
+    return lay
+
+
+def grid(F=5, H=64, W=80):
+    return hv.hv_token_grid(F, H, W)._c()   # 2 x 4 x 5 = 40 video tokens
+
+
+def rope(q=FAKE, k=FAKE + SEP, lay=None, g=None, theta=10000.0):
+    lib = hv.load_library()
+    lay = layout() if lay is None else lay
+    g = grid() if g is None else g
+    return lib.hv_rope3d_apply(q, k, ctypes.byref(lay) if lay is not False else None,
+                               ctypes.byref(g) if g is not False else None, theta, None)
+
+
+def attn(q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP, out=FAKE + 3 * SEP, valid=(10,), lay=None,
+         n_video=40, scale=0.0):
+    lib = hv.load_library()
+    lay = layout() if lay is None else lay
+    arr = None if valid is None else (ctypes.c_int32 * max(1, len(valid)))(*valid)
+    return lib.hv_joint_attention_fwd(q, k, v, arr, out, ctypes.byref(lay) if lay is not False else None,
+                                      n_video, scale, None)
+
+
+E, U = hv.HV_ERR_INVALID_ARG, hv.HV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(k=0), E), (dict(lay=False), E), (dict(g=False), E),
+    (dict(q=FAKE + 2), E), (dict(k=FAKE + SEP + 8), E),
+    (dict(k=FAKE + 3072 * 2), E),                         # k overlaps q
+    (dict(theta=0.0), E), (dict(theta=-1.0), E), (dict(theta=float("nan")), E), (dict(theta=float("inf")), E),
+    (dict(lay=layout(heads=16)), U), (dict(lay=layout(dim=64)), U),
+    (dict(lay=layout(batch=65)), U),
+    (dict(lay=layout(seq=(1 << 24) + 1)), U),
+    (dict(lay=layout(batch=-1)), E), (dict(lay=layout(seq=-5)), E),
+    (dict(lay=layout(sl=3000)), E), (dict(lay=layout(sl=3076)), E),
+    (dict(lay=layout(batch=2, sb=3072 * 10)), E),         # batch stride too small
+    (dict(lay=layout(seq=39)), E),                        # fewer rows than video tokens
+])
+def test_rope_validation(kwargs, expect):
+    assert rope(**kwargs) == expect
+
+
+def test_rope_inconsistent_grid():
+    g = grid()
+    g.n_video = 41
+    assert rope(g=g) == E
+    g = grid()
+    g.gw = 0
+    assert rope(g=g) == E
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(k=0), E), (dict(v=0), E), (dict(out=0), E), (dict(lay=False), E),
+    (dict(v=FAKE + 2 * SEP + 4), E), (dict(out=FAKE + 3 * SEP + 2), E),
+    (dict(out=FAKE + 100 * 3072 * 2), E),                 # out overlaps q
+    (dict(out=FAKE + SEP - 64), E),                       # out overlaps the start of k
+    (dict(out=FAKE + 2 * SEP + 299 * 3072 * 2), E),       # out overlaps the last row of v
+    (dict(valid=(-1,)), E), (dict(valid=(261,)), E),      # text capacity is 300 - 40 = 260
+    (dict(n_video=-1), E), (dict(n_video=301), E),
+    (dict(n_video=0, valid=(0,)), E),                     # no valid key
+    (dict(lay=layout(heads=32)), U), (dict(lay=layout(dim=256)), U),
+    (dict(lay=layout(batch=65), valid=None), U),
+    (dict(lay=layout(sl=3080 + 4)), E),
+    (dict(lay=layout(batch=2, sb=3072 * 299), valid=(1, 1)), E),
+])
+def test_attention_validation(kwargs, expect):
+    assert attn(**kwargs) == expect
+
+
+def test_attention_second_batch_entry_checked():
+    assert attn(lay=layout(batch=3, seq=300), valid=(10, 10, 999)) == E
+    assert attn(lay=layout(batch=3, seq=300), valid=(10, -2, 5)) == E
+
+
+def test_empty_calls_are_noops():
+    # batch 0 or seq 0: nothing to compute, no launch (so no GPU needed)
+    assert attn(lay=layout(batch=0), valid=None, n_video=0) == hv.HV_OK
+    assert attn(lay=layout(seq=0, sb=0), valid=(0,), n_video=0) == hv.HV_OK
+    assert rope(lay=layout(batch=0)) == hv.HV_OK
