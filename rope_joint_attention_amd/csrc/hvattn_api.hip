@@ -33,10 +33,24 @@ int check_layout(const hv_layout* lay, int64_t* extent) {
   return HV_OK;
 }
 
-bool overlap(const void* a, const void* b, int64_t elems) {
+// Do two tensors with the same layout, based at a and b, share an element?
+// Disjoint address ranges never do.  Otherwise, when every row starts at a
+// multiple of stride_l (one batch entry, or stride_b a multiple of stride_l),
+// the rows of b sit at a fixed offset r (mod stride_l) from the rows of a and
+// the tensors are disjoint exactly when both row segments fit side by side:
+// r >= 3072 and stride_l - r >= 3072 (e.g. q, k, v sliced from one fused
+// [B][L][3][24][128] buffer).  Any other overlapping case counts as aliasing.
+bool overlap(const void* a, const void* b, const hv_layout* lay, int64_t elems) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   const uintptr_t n = (uintptr_t)elems * sizeof(hv_bf16);
-  return x < y + n && y < x + n;
+  if (!(x < y + n && y < x + n)) return false;
+  const uintptr_t dbytes = x > y ? x - y : y - x;
+  if (dbytes % sizeof(hv_bf16) != 0) return true;
+  const int64_t d = (int64_t)(dbytes / sizeof(hv_bf16));
+  const int64_t sl = lay->stride_l;
+  if (lay->batch > 1 && lay->stride_b % sl != 0) return true;
+  const int64_t r = d % sl;
+  return !(r >= kRowElems && sl - r >= kRowElems);
 }
 
 int check_grid(const hv_grid* g) {
@@ -94,7 +108,7 @@ int hv_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout, const hv_gr
   if (grid->n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
   if (!q || !k) return HV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k)) return HV_ERR_INVALID_ARG;
-  if (overlap(q, k, extent)) return HV_ERR_INVALID_ARG;
+  if (overlap(q, k, layout, extent)) return HV_ERR_INVALID_ARG;
   if (layout->batch == 0 || layout->seq_len == 0 || grid->n_video == 0) return HV_OK;
 
   hv::RopeParams p;
@@ -127,7 +141,8 @@ int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
   if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
   if (!q || !k || !v || !out) return HV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HV_ERR_INVALID_ARG;
-  if (overlap(out, q, extent) || overlap(out, k, extent) || overlap(out, v, extent))
+  if (overlap(out, q, layout, extent) || overlap(out, k, layout, extent) ||
+      overlap(out, v, layout, extent))
     return HV_ERR_INVALID_ARG;
   if (layout->batch == 0 || layout->seq_len == 0) return HV_OK;
 

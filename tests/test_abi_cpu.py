@@ -178,3 +178,23 @@ def test_empty_calls_are_noops():
     assert attn(lay=layout(batch=0), valid=None, n_video=0) == hv.HV_OK
     assert attn(lay=layout(seq=0, sb=0), valid=(0,), n_video=0) == hv.HV_OK
     assert rope(lay=layout(batch=0)) == hv.HV_OK
+
+
+@pytest.mark.parametrize("delta_elems,sl,batch,sb", [
+    (1024, 9216, 1, None),        # rows of k start 1024 channels into q's rows
+    (7000, 9216, 1, None),        # k's row would run into q's next row
+    (9216 * 5, 9216, 1, None),    # same rows, five tokens later
+    (3072, 9216, 2, 9216 * 300 + 8),  # batch stride not a multiple of the token stride
+])
+def test_interleaved_views_that_alias_are_rejected(delta_elems, sl, batch, sb):
+    lay = layout(batch=batch, sl=sl, sb=sb)
+    assert rope(k=FAKE + 2 * delta_elems, lay=lay) == E
+    valid = (10,) * batch
+    assert attn(out=FAKE + SEP + 2 * delta_elems, lay=lay, valid=valid) == E
+
+
+def test_odd_byte_offset_counts_as_aliasing():
+    lay = layout(sl=9216)
+    # 16-byte aligned but an odd element offset is impossible; an unaligned
+    # pointer is rejected first, by the alignment rule
+    assert rope(k=FAKE + 2 * 3072 + 1, lay=lay) == E
