@@ -31,6 +31,8 @@
 // The padded-key mask is a loop bound plus a predicate on the last tile;
 // K and V rows at or beyond the valid length are never read (zeros are
 // staged instead), so garbage in padded rows cannot reach the output.
+#include <type_traits>
+
 #include "hv_internal.h"
 
 namespace hv {
@@ -85,9 +87,65 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-struct Stage {
-  u32x4 k0, k1, v0, v1;
+// ---- scheduling hints -------------------------------------------------------
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
+constexpr int kSchedDSWrite = 0x200;
+constexpr int kSchedVMEMRead = 0x020;
+#ifndef HV_ATTN_SCHED
+#define HV_ATTN_SCHED 1
+#endif
+#if HV_ATTN_SCHED
+#define HV_SCHED_GROUP(mask, n, id) __builtin_amdgcn_sched_group_barrier(mask, n, id)
+#else
+#define HV_SCHED_GROUP(mask, n, id) ((void)0)
+#endif
+
+// ---- per-step building blocks --------------------------------------------------
+
+struct KStage {
+  u32x4 r0, r1;
 };
+struct VStage {
+  u32x4 a, b;
+};
+
+// Row maximum of a score tile (32 in-lane values, then across the two halves),
+// in the log2 domain.  Masked keys must already be -inf.
+__device__ __forceinline__ float tile_max(const f32x16& s0, const f32x16& s1, float c2) {
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+  return max_across_halves(mx) * c2;
+}
+
+__device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int lim, int hh) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
+    if (key >= lim) s0[v] = -INFINITY;
+    if (key + 32 >= lim) s1[v] = -INFINITY;
+  }
+}
+
+// Raise the running reference to the tile maximum when it exceeds it by more
+// than 2^8; rescale the accumulators accordingly (rare after the first tiles).
+__device__ __forceinline__ void update_reference(float mx, float& m_run, float& l_run,
+                                                 f32x16 (&o)[4]) {
+  const bool need = mx > m_run + kRescaleLog2;
+  if (__any(need)) {
+    const float m_new = need ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+  }
+}
 
 __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KS];
@@ -137,29 +195,48 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const int k_c = tid & 15;
   const int v_kp = lane & 31;
   const int v_c = wave * 2 + hh;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  auto load_stage = [&](int tile, Stage& st) {
-    const int kb = tile * BN;
-    const int r0 = kb + k_row, r1 = r0 + 32;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    st.k0 = r0 < Lk ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)r0 * sl + k_c * 8) : zero;
-    st.k1 = r1 < Lk ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)r1 * sl + k_c * 8) : zero;
-    const int v0r = kb + 2 * v_kp, v1r = v0r + 1;
-    st.v0 = v0r < Lk ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)v0r * sl + v_c * 8) : zero;
-    st.v1 = v1r < Lk ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)v1r * sl + v_c * 8) : zero;
+  // K rows past the valid keys are clamped to the last valid row: they are
+  // always in bounds, and their scores are replaced by -inf on the last tile.
+  // V rows past the valid keys (last tile only) are clamped and zeroed, so
+  // padding contents (even NaN) never meet a zero weight.
+  auto load_k = [&](int tile, KStage& st) {
+    const int r0 = min(tile * BN + k_row, Lk - 1), r1 = min(tile * BN + k_row + 32, Lk - 1);
+    st.r0 = *reinterpret_cast<const u32x4*>(Kg + (int64_t)r0 * sl + k_c * 8);
+    st.r1 = *reinterpret_cast<const u32x4*>(Kg + (int64_t)r1 * sl + k_c * 8);
   };
-
-  auto store_stage = [&](int buf, const Stage& st) {
-    *reinterpret_cast<u32x4*>(&sK[buf][k_row * KS + k_c * 8]) = st.k0;
-    *reinterpret_cast<u32x4*>(&sK[buf][(k_row + 32) * KS + k_c * 8]) = st.k1;
+  auto store_k = [&](int buf, const KStage& st) {
+    *reinterpret_cast<u32x4*>(&sK[buf][k_row * KS + k_c * 8]) = st.r0;
+    *reinterpret_cast<u32x4*>(&sK[buf][(k_row + 32) * KS + k_c * 8]) = st.r1;
+  };
+  auto load_v = [&](int tile, VStage& st) {  // tile fully inside the valid keys
+    const int r0 = tile * BN + 2 * v_kp;
+    st.a = *reinterpret_cast<const u32x4*>(Vg + (int64_t)r0 * sl + v_c * 8);
+    st.b = *reinterpret_cast<const u32x4*>(Vg + (int64_t)(r0 + 1) * sl + v_c * 8);
+  };
+  auto load_v_last = [&](int tile, VStage& st) {  // may run past the valid keys
+    const int r0 = tile * BN + 2 * v_kp, r1 = r0 + 1;
+    st.a = *reinterpret_cast<const u32x4*>(Vg + (int64_t)min(r0, Lk - 1) * sl + v_c * 8);
+    st.b = *reinterpret_cast<const u32x4*>(Vg + (int64_t)min(r1, Lk - 1) * sl + v_c * 8);
+    if (r0 >= Lk) st.a = zero;
+    if (r1 >= Lk) st.b = zero;
+  };
+  auto store_v = [&](int buf, const VStage& st) {
     uint32_t* vt = reinterpret_cast<uint32_t*>(&sV[buf][0]);
     const int col = vt_pos(2 * v_kp);  // even: keys 2kp, 2kp+1 are adjacent
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t a = st.v0[e >> 1], c = st.v1[e >> 1];
+      const uint32_t a = st.a[e >> 1], c = st.b[e >> 1];
       const uint32_t w = (e & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
       vt[((8 * v_c + e) * VS + col) >> 1] = w;
     }
+  };
+  auto k_frag = [&](const uint16_t* kt, int half, int kc) {
+    return *reinterpret_cast<const bf16x8*>(kt + (half * 32 + l32) * KS + kc * 16 + hh * 8);
+  };
+  auto v_frag = [&](const uint16_t* vt, int dt, int mm) {
+    return *reinterpret_cast<const bf16x8*>(vt + (dt * 32 + l32) * VS + mm * 16 + hh * 8);
   };
 
   f32x16 o[4];
@@ -168,88 +245,162 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
   float m_run = -INFINITY;  // running reference, log2 domain
-  float l_run = 0.f;        // this lane's share of the softmax denominator
+  float l_run = 0.f;        // this lane's share of the denominator (bf16-rounded weights)
   const float c2 = p.scale_log2;
-
   const int ntiles = (Lk + BN - 1) / BN;
-  Stage st;
-  load_stage(0, st);
-  store_stage(0, st);
-  __syncthreads();
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_stage(t + 1, st);
-
-    // ---- S^T = K Q^T for the two 32-key halves of the tile
-    f32x16 s0, s1;
+  // exp2 of scores e0, e0+1 of tile registers s (in place)
+  auto exp_pair = [&](f32x16 (&s)[2], int e0) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
-    const uint16_t* kt = &sK[buf][0];
+    for (int e = e0; e < e0 + 2; ++e)
+      s[e >> 4][e & 15] = __builtin_amdgcn_exp2f(fmaf(s[e >> 4][e & 15], c2, -m_run));
+  };
+  // bf16 P^T operand for keys 16*i .. 16*i+15 and its share of the denominator.
+  // The four packed words are built as separate 32-bit values and fed to
+  // v_dot2 before they are assembled into the MFMA operand: taking them back
+  // out of the 128-bit operand (as vector elements) makes this compiler encode
+  // the first word for all four v_dot2c_f32_bf16 operands.
+  auto pack_p = [&](f32x16 (&s)[2], int i) {
+    const f32x16& src = s[i >> 1];
+    const int base = (i & 1) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack_bf16(src[base + 2 * j], src[base + 2 * j + 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, l_run, false);
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+
+  // ---- prologue: K tiles 0 and 1, V tile 0; scores and reference of tile 0
+  {
+    KStage ks;
+    VStage vs;
+    load_k(0, ks);
+    if (ntiles == 1) load_v_last(0, vs); else load_v(0, vs);
+    store_k(0, ks);
+    store_v(0, vs);
+    if (ntiles > 1) {
+      load_k(1, ks);
+      store_k(1, ks);
+    }
+  }
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) { sa[0][v] = 0.f; sa[1][v] = 0.f; }
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(&sK[0][0], 0, kc), qf[kc], sa[0], 0, 0, 0);
+    sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(&sK[0][0], 1, kc), qf[kc], sa[1], 0, 0, 0);
+  }
+  if (ntiles == 1) mask_tile(sa[0], sa[1], Lk, hh);
+  update_reference(tile_max(sa[0], sa[1], c2), m_run, l_run, o);
+  __syncthreads();  // every wave has read K tile 0 before its buffer is refilled
+
+  // ---- steady state.  Step t (tile t+1 exists):
+  //   phase 1: QK^T MFMAs of tile t+1, interleaved with the exp2 / bf16 / sum
+  //            work of tile t (independent VALU that runs under the MFMAs);
+  //   phase 2: PV MFMAs of tile t, interleaved with the row maximum of tile t+1;
+  //   then the staged K tile t+2 and V tile t+1 go to the free LDS buffers,
+  //   one barrier, and the reference update for tile t+1 (rarely taken).
+  auto step = [&](auto last, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr bool kLast = decltype(last)::value;  // tile t+1 is the last tile
+    KStage ks;
+    VStage vs;
+    if constexpr (!kLast) {
+      load_k(t + 2, ks);
+      load_v(t + 1, vs);
+    } else {
+      load_v_last(t + 1, vs);
+    }
+    const uint16_t* kt = &sK[(t + 1) & 1][0];
+    const uint16_t* vt = &sV[t & 1][0];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { nxt[0][v] = 0.f; nxt[1][v] = 0.f; }
+    bf16x8 pb[4];
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + l32 * KS + kc * 16 + hh * 8);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + (l32 + 32) * KS + kc * 16 + hh * 8);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kc], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kc], s1, 0, 0, 0);
+      nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, 0, kc), qf[kc], nxt[0], 0, 0, 0);
+      exp_pair(cur, 4 * kc);
+      nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, 1, kc), qf[kc], nxt[1], 0, 0, 0);
+      exp_pair(cur, 4 * kc + 2);
+      if (kc & 1) pb[kc >> 1] = pack_p(cur, kc >> 1);
+    }
+    HV_SCHED_GROUP(kSchedVMEMRead, 4, 0);
+    HV_SCHED_GROUP(kSchedDSRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      HV_SCHED_GROUP(kSchedMFMA, 1, 0);
+      HV_SCHED_GROUP(kSchedVALU, 6, 0);
+      HV_SCHED_GROUP(kSchedDSRead, 1, 0);
+      HV_SCHED_GROUP(kSchedMFMA, 1, 0);
+      HV_SCHED_GROUP(kSchedVALU, 6, 0);
+      HV_SCHED_GROUP(kSchedDSRead, 1, 0);
     }
 
-    // ---- padded keys of the last tile: s = -inf
-    const int lim = Lk - t * BN;
-    if (lim < BN) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (key >= lim) s0[v] = -INFINITY;
-        if (key + 32 >= lim) s1[v] = -INFINITY;
-      }
-    }
+    if constexpr (kLast) mask_tile(nxt[0], nxt[1], Lk - (t + 1) * BN, hh);
 
-    // ---- row maximum (16 + 16 values in lane, then across the halves)
-    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-    mx = max_across_halves(mx) * c2;
-
-    const bool need = mx > m_run + kRescaleLog2;
-    if (__any(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vt, dt, mm), pb[mm], o[dt], 0, 0, 0);
+    const float mx = tile_max(nxt[0], nxt[1], c2);
+    if constexpr (!kLast) store_k(t & 1, ks);
+    store_v((t + 1) & 1, vs);
+    HV_SCHED_GROUP(kSchedDSRead, 4, 1);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
+    for (int i = 0; i < 4; ++i) {
+      HV_SCHED_GROUP(kSchedMFMA, 1, 1);
+      HV_SCHED_GROUP(kSchedDSRead, 1, 1);
     }
-
-    // ---- probabilities p = 2^(s*c2 - m)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s0[v] = __builtin_amdgcn_exp2f(fmaf(s0[v], c2, -m_run));
-      s1[v] = __builtin_amdgcn_exp2f(fmaf(s1[v], c2, -m_run));
-      l_run += s0[v] + s1[v];
+    for (int i = 0; i < 12; ++i) {
+      HV_SCHED_GROUP(kSchedMFMA, 1, 1);
+      HV_SCHED_GROUP(kSchedVALU, 3, 1);
+      HV_SCHED_GROUP(kSchedDSRead, 1, 1);
     }
-    bf16x8 pb[4];
-    pb[0] = to_bf16x8(s0, 0);
-    pb[1] = to_bf16x8(s0, 8);
-    pb[2] = to_bf16x8(s1, 0);
-    pb[3] = to_bf16x8(s1, 8);
-
-    // ---- O^T += V^T P^T, 16 keys per MFMA
-    const uint16_t* vt = &sV[buf][0];
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (dt * 32 + l32) * VS + mm * 16 + hh * 8);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mm], o[dt], 0, 0, 0);
-      }
-    }
-
-    if (has_next) store_stage(buf ^ 1, st);
+    HV_SCHED_GROUP(kSchedDSWrite, 10, 1);
     __syncthreads();
+    update_reference(mx, m_run, l_run, o);
+  };
+
+  using Plain = std::integral_constant<bool, false>;
+  using Last = std::integral_constant<bool, true>;
+  int t = 0;
+  for (; t + 3 < ntiles; t += 2) {
+    step(Plain{}, t, sa, sb);
+    step(Plain{}, t + 1, sb, sa);
+  }
+  if (t + 2 < ntiles) {
+    step(Plain{}, t, sa, sb);
+    step(Last{}, t + 1, sb, sa);
+    t += 2;
+  } else if (t + 1 < ntiles) {
+    step(Last{}, t, sa, sb);
+    ++t;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { sa[0][v] = sb[0][v]; sa[1][v] = sb[1][v]; }
+  }
+
+  // ---- last tile: softmax and PV only
+  {
+    const uint16_t* vt = &sV[t & 1][0];
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      exp_pair(sa, 4 * kc);
+      exp_pair(sa, 4 * kc + 2);
+      if (kc & 1) pb[kc >> 1] = pack_p(sa, kc >> 1);
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vt, dt, mm), pb[mm], o[dt], 0, 0, 0);
   }
 
   // ---- epilogue: O / l, round to bf16, store rows that exist
