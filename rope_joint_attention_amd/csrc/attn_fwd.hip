@@ -8,29 +8,36 @@
 // never written to memory.
 //
 // Work decomposition
-//   * one workgroup = (batch, head, 256 query rows); 8 waves, 32 rows each,
-//     two waves per SIMD so one wave's softmax overlaps the other's MFMA;
-//   * key/value tiles of 64 rows are staged through LDS, double buffered:
-//     the next tile's global loads are issued before the current tile's
-//     math and written to the other LDS buffer after it;
+//   * one workgroup = (batch, head, 256 query rows); 8 waves of 32 rows, two
+//     waves per SIMD;
+//   * K and V tiles of 64 keys reach LDS by direct global->LDS loads
+//     (global_load_lds_dwordx4: no registers, fully coalesced 1 KB per wave
+//     instruction) into three LDS stages, each tile requested two steps
+//     before it is used;
 //   * workgroup ids are remapped so that consecutive query blocks of one
 //     (batch, head) run on the same XCD and share its L2 for K/V.
 //
-// Per wave and tile, in MFMA 32x32x16 bf16 (fp32 accumulate):
+// Per wave and step, in MFMA 32x32x16 bf16 (fp32 accumulate):
 //   S^T (64 keys x 32 queries) = K_tile * Q^T   -- lane l owns query l%32, so
 //       row statistics are 32 in-register values plus one exchange between
 //       the two 32-lane halves (v_permlane32_swap);
 //   online softmax in the log2 domain with exp2; the running reference m is
 //       only raised when a row maximum exceeds it by more than 8 (factor 256),
-//       which keeps every probability <= 256 and the result exact, while
+//       which keeps every probability <= 256 and the result exact while
 //       skipping almost all accumulator rescales;
 //   O^T (128 channels x 32 queries) += V^T_tile * P^T -- P^T stays in the
-//       registers the softmax produced (converted to bf16); V is written to
-//       LDS transposed, with the key order inside each 16-key group permuted
-//       to match the register layout of P^T.
-// The padded-key mask is a loop bound plus a predicate on the last tile;
-// K and V rows at or beyond the valid length are never read (zeros are
-// staged instead), so garbage in padded rows cannot reach the output.
+//       registers the softmax produced (bf16); V stays in its natural
+//       [key][channel] layout in LDS and the MFMA operand is gathered with
+//       the gfx950 transposing read ds_read_b64_tr_b16 (two per operand).
+//   The step is software-pipelined: the QK^T MFMAs of tile t+1 run under the
+//   softmax VALU work of tile t, the PV MFMAs of tile t under the row maximum
+//   of tile t+1.
+// LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled within a row (K:
+// slot c ^ (r % 16), V: slot c ^ 4(r % 4)) so that both the K operand reads and
+// the transposing V reads run without bank conflicts.  The padded-key mask is a loop bound plus a predicate on
+// the last tile.  Rows past the valid keys are never read: their loads are
+// clamped to the last valid row, whose scores are masked to -inf (K) or whose
+// weights are exactly zero (V), so padding contents cannot reach the output.
 #include <type_traits>
 
 #include "hv_internal.h"
@@ -40,10 +47,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define HV_LDS __attribute__((address_space(3)))
 
 constexpr int D = HV_HEAD_DIM;  // 128
 constexpr int BN = 64;          // keys per tile
@@ -51,17 +60,27 @@ constexpr int NW = 8;           // waves per workgroup
 constexpr int QPW = 32;         // query rows per wave
 constexpr int BM = NW * QPW;    // 256 query rows per workgroup
 constexpr int NT = NW * 64;     // 512 threads
-constexpr int KS = D + 8;       // K tile row stride in LDS (bf16): 272 B, conflict-free reads
-constexpr int VS = BN + 8;      // V^T tile row stride in LDS (bf16): 144 B
+constexpr int NSTAGE = 3;       // K/V tiles resident in LDS
+constexpr int ROWB = D * 2;     // bytes per K/V row in LDS (no padding; swizzled)
+constexpr int TILEB = BN * ROWB;                 // 16 KB per K or V tile
+constexpr int LDS_BYTES = 2 * NSTAGE * TILEB;    // 96 KB
 constexpr float kRescaleLog2 = 8.0f;
 
-// Position of key `key` (0..63 inside a tile) in a V^T row.  Inside every
-// group of 16 keys, bits 2 and 3 of the key index are swapped: the P^T
-// operand register of lane-half h, slot e holds key 8*(e/4) + 4h + e%4 of its
-// 16-key group, so V^T must hold that key at position 8h + e.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+// s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt
+// [6:4] (left at its maximum), lgkmcnt [11:8].
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
+
+// Byte offset of 16-byte chunk c of row r inside a K tile: slot c ^ (r % 16).
+// The 16-byte K operand reads take 16 consecutive rows at one chunk: they hit
+// all 16 slots.
+__device__ __forceinline__ int kswz(int r, int c) { return r * ROWB + ((c ^ (r & 15)) << 4); }
+// Same for a V tile: slot c ^ 4(r % 4).  One transposing read covers 8
+// consecutive rows (a multiple of 8 onwards) and 4 consecutive chunks (a
+// multiple of 4 onwards): 32 (row, chunk) pairs that land on every slot
+// exactly twice, the minimum for 512 bytes.
+__device__ __forceinline__ int vswz(int r, int c) { return r * ROWB + ((c ^ ((r & 3) << 2)) << 4); }
 
 __device__ __forceinline__ float max_across_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -78,22 +97,24 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& s, int base) {
-  u32x4 w;
-  w.x = pack_bf16(s[base + 0], s[base + 1]);
-  w.y = pack_bf16(s[base + 2], s[base + 3]);
-  w.z = pack_bf16(s[base + 4], s[base + 5]);
-  w.w = pack_bf16(s[base + 6], s[base + 7]);
-  return __builtin_bit_cast(bf16x8, w);
+// Workgroup barrier without the memory fence __syncthreads() implies: the
+// fence would drain the in-flight global->LDS loads of later tiles.  The
+// caller waits for exactly the loads and LDS operations that must be
+// complete; the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+template <int kVm>
+__device__ __forceinline__ void barrier_after(void) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kVm, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---- scheduling hints -------------------------------------------------------
-// Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedVALU = 0x002;
 constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedDSRead = 0x100;
-constexpr int kSchedDSWrite = 0x200;
 constexpr int kSchedVMEMRead = 0x020;
+constexpr int kSchedDSRead = 0x100;
 #ifndef HV_ATTN_SCHED
 #define HV_ATTN_SCHED 1
 #endif
@@ -102,15 +123,6 @@ constexpr int kSchedVMEMRead = 0x020;
 #else
 #define HV_SCHED_GROUP(mask, n, id) ((void)0)
 #endif
-
-// ---- per-step building blocks --------------------------------------------------
-
-struct KStage {
-  u32x4 r0, r1;
-};
-struct VStage {
-  u32x4 a, b;
-};
 
 // Row maximum of a score tile (32 in-lane values, then across the two halves),
 // in the log2 domain.  Masked keys must already be -inf.
@@ -148,8 +160,7 @@ __device__ __forceinline__ void update_reference(float mx, float& m_run, float& 
 }
 
 __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VS];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -187,56 +198,89 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     for (int kc = 0; kc < 8; ++kc) qf[kc] = *reinterpret_cast<const bf16x8*>(qptr + kc * 16);
   }
 
-  // Staging roles.  K: thread -> rows (tid/16, tid/16 + 32), 16-byte chunk tid%16
-  // (coalesced).  V: lane -> key pair (lane%32), channel chunk 2*wave + lane/32,
-  // so that the transposed LDS writes of a wave cover 32 consecutive dwords
-  // in two rows 8 channels apart (no bank conflicts).
-  const int k_row = tid >> 4;
-  const int k_c = tid & 15;
-  const int v_kp = lane & 31;
-  const int v_c = wave * 2 + hh;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // ---- global -> LDS tile loads.  A tile is 16 wave instructions of 4 rows
+  // (1 KB); wave w issues instructions 2w and 2w+1 of each K and V tile.
+  // Lane l of an instruction fills LDS slot l%16 of row 4i + l/16, i.e. it
+  // loads chunk (l%16) ^ (row%16) of that row: the swizzle costs nothing and
+  // the 16 lanes of a row still read its 256 contiguous bytes.
+  const int ld_row0 = 8 * wave + (lane >> 4);        // first instruction's row
+  const int ld_kc0 = (lane & 15) ^ (ld_row0 & 15);   // K chunk landing in slot lane%16
+  const int ld_kc1 = (lane & 15) ^ ((ld_row0 + 4) & 15);
+  const int ld_vc = (lane & 15) ^ ((ld_row0 & 3) << 2);  // V: rows r and r+4 swizzle alike
+  // Row offsets are 32-bit byte offsets from the tile's first row (a tile
+  // spans 64 rows, far below 4 GB); only rows past the valid keys, in the
+  // last tile, get clamped.
+  const uint32_t row_bytes = (uint32_t)(sl * 2);
+  auto load_tile = [&](const uint16_t* g, int buf_off, int tile, int c0, int c1) {
+    const int lim = Lk - 1 - tile * BN;  // last valid row, relative to the tile
+    const uint32_t o0 = (uint32_t)min(ld_row0, lim) * row_bytes + c0 * 16;
+    const uint32_t o1 = (uint32_t)min(ld_row0 + 4, lim) * row_bytes + c1 * 16;
+    const unsigned char* tb = (const unsigned char*)(g + (int64_t)tile * BN * sl);
+    HV_LDS void* dst = (HV_LDS void*)(lds + buf_off + wave * 2048);
+    __builtin_amdgcn_global_load_lds(tb + o0, dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(tb + o1, (HV_LDS unsigned char*)dst + 1024, 16, 0, 0);
+  };
+  auto load_k = [&](int buf_off, int tile) { load_tile(Kg, buf_off, tile, ld_kc0, ld_kc1); };
+  auto load_v = [&](int buf_off, int tile) { load_tile(Vg, buf_off, tile, ld_vc, ld_vc); };
+  auto k_off = [](int stage) { return stage * TILEB; };
+  auto v_off = [](int stage) { return (NSTAGE + stage) * TILEB; };
 
-  // K rows past the valid keys are clamped to the last valid row: they are
-  // always in bounds, and their scores are replaced by -inf on the last tile.
-  // V rows past the valid keys (last tile only) are clamped and zeroed, so
-  // padding contents (even NaN) never meet a zero weight.
-  auto load_k = [&](int tile, KStage& st) {
-    const int r0 = min(tile * BN + k_row, Lk - 1), r1 = min(tile * BN + k_row + 32, Lk - 1);
-    st.r0 = *reinterpret_cast<const u32x4*>(Kg + (int64_t)r0 * sl + k_c * 8);
-    st.r1 = *reinterpret_cast<const u32x4*>(Kg + (int64_t)r1 * sl + k_c * 8);
-  };
-  auto store_k = [&](int buf, const KStage& st) {
-    *reinterpret_cast<u32x4*>(&sK[buf][k_row * KS + k_c * 8]) = st.r0;
-    *reinterpret_cast<u32x4*>(&sK[buf][(k_row + 32) * KS + k_c * 8]) = st.r1;
-  };
-  auto load_v = [&](int tile, VStage& st) {  // tile fully inside the valid keys
-    const int r0 = tile * BN + 2 * v_kp;
-    st.a = *reinterpret_cast<const u32x4*>(Vg + (int64_t)r0 * sl + v_c * 8);
-    st.b = *reinterpret_cast<const u32x4*>(Vg + (int64_t)(r0 + 1) * sl + v_c * 8);
-  };
-  auto load_v_last = [&](int tile, VStage& st) {  // may run past the valid keys
-    const int r0 = tile * BN + 2 * v_kp, r1 = r0 + 1;
-    st.a = *reinterpret_cast<const u32x4*>(Vg + (int64_t)min(r0, Lk - 1) * sl + v_c * 8);
-    st.b = *reinterpret_cast<const u32x4*>(Vg + (int64_t)min(r1, Lk - 1) * sl + v_c * 8);
-    if (r0 >= Lk) st.a = zero;
-    if (r1 >= Lk) st.b = zero;
-  };
-  auto store_v = [&](int buf, const VStage& st) {
-    uint32_t* vt = reinterpret_cast<uint32_t*>(&sV[buf][0]);
-    const int col = vt_pos(2 * v_kp);  // even: keys 2kp, 2kp+1 are adjacent
+  // Operand addresses.  The swizzle only depends on the row modulo 16, so
+  // moving 16 rows (V key groups) or 32 rows (K halves) is a plain immediate
+  // offset; the lane-dependent XOR is folded into 16 per-lane offsets computed
+  // once.  A step only adds the stage base to them.
+  //
+  // K operand (rows half*32 + l32, channel chunk 2kc + hh): one 16-byte read.
+  int koff[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t a = st.a[e >> 1], c = st.b[e >> 1];
-      const uint32_t w = (e & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
-      vt[((8 * v_c + e) * VS + col) >> 1] = w;
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = kswz(l32, 2 * kc + hh);
+  // V^T operand for channels 32dt + l32 and keys 16mm + 8(e/4) + 4hh + e%4
+  // (slot e), matching the register layout of P^T.  ds_read_b64_tr_b16: in each
+  // group of 16 lanes, lane j receives element j%4 of the 8-byte rows that
+  // lanes j/4, j/4+4, j/4+8, j/4+12 address.  Lane p of a group addresses key
+  // (base + p/4), channels d0 + 4(p%4) .. +3, so lane j ends up with channel
+  // d0 + j of keys base .. base+3.
+  int voff[8];
+  {
+    const int tr_key = 4 * hh + ((lane & 15) >> 2);
+    const int tr_ch = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ch = 32 * dt + tr_ch;
+        voff[2 * dt + q] = vswz(tr_key + 8 * q, ch >> 3) + 2 * (ch & 7);
+      }
+  }
+  // Per-step operand bases: stage base + per-lane offset.  The empty asm makes
+  // each base opaque, so the compiler keeps the 16 bases in registers and
+  // folds the K-half / V-key-group offsets into the ds_read immediates rather
+  // than hoisting every (offset + immediate) sum out of the loop.
+  struct Bases {
+    uint32_t k[8], v[8];
+  };
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(HV_LDS unsigned char*)lds;
+  auto bases = [&](int kstage, int vstage) {
+    Bases bs;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bs.k[i] = lds_base + k_off(kstage) + koff[i];
+      bs.v[i] = lds_base + v_off(vstage) + voff[i];
+      asm volatile("" : "+v"(bs.k[i]), "+v"(bs.v[i]));
     }
+    return bs;
   };
-  auto k_frag = [&](const uint16_t* kt, int half, int kc) {
-    return *reinterpret_cast<const bf16x8*>(kt + (half * 32 + l32) * KS + kc * 16 + hh * 8);
+  auto k_frag = [&](const Bases& bs, int half, int kc) {
+    return *(const HV_LDS bf16x8*)(uintptr_t)(bs.k[kc] + half * 32 * ROWB);
   };
-  auto v_frag = [&](const uint16_t* vt, int dt, int mm) {
-    return *reinterpret_cast<const bf16x8*>(vt + (dt * 32 + l32) * VS + mm * 16 + hh * 8);
+  auto v_frag = [&](const Bases& bs, int dt, int mm) {
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (HV_LDS i16x4*)(uintptr_t)(bs.v[2 * dt] + mm * 16 * ROWB));
+    const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (HV_LDS i16x4*)(uintptr_t)(bs.v[2 * dt + 1] + mm * 16 * ROWB));
+    const u32x4 w = {__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1],
+                     __builtin_bit_cast(u32x2, c)[0], __builtin_bit_cast(u32x2, c)[1]};
+    return __builtin_bit_cast(bf16x8, w);
   };
 
   f32x16 o[4];
@@ -274,97 +318,100 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     return __builtin_bit_cast(bf16x8, v);
   };
 
-  // ---- prologue: K tiles 0 and 1, V tile 0; scores and reference of tile 0
-  {
-    KStage ks;
-    VStage vs;
-    load_k(0, ks);
-    if (ntiles == 1) load_v_last(0, vs); else load_v(0, vs);
-    store_k(0, ks);
-    store_v(0, vs);
-    if (ntiles > 1) {
-      load_k(1, ks);
-      store_k(1, ks);
-    }
-  }
-  __syncthreads();
+  // ---- prologue: K tiles 0..2 and V tiles 0..1 requested; scores of tile 0
+  load_k(k_off(0), 0);
+  load_k(k_off(1), min(1, ntiles - 1));
+  load_k(k_off(2), min(2, ntiles - 1));
+  load_v(v_off(0), 0);
+  load_v(v_off(1), min(1, ntiles - 1));
+  barrier_after<0>();
   f32x16 sa[2], sb[2];
+  const Bases b0 = bases(0, 0);
 #pragma unroll
   for (int v = 0; v < 16; ++v) { sa[0][v] = 0.f; sa[1][v] = 0.f; }
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
-    sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(&sK[0][0], 0, kc), qf[kc], sa[0], 0, 0, 0);
-    sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(&sK[0][0], 1, kc), qf[kc], sa[1], 0, 0, 0);
+    sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(b0, 0, kc), qf[kc], sa[0], 0, 0, 0);
+    sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(b0, 1, kc), qf[kc], sa[1], 0, 0, 0);
   }
   if (ntiles == 1) mask_tile(sa[0], sa[1], Lk, hh);
   update_reference(tile_max(sa[0], sa[1], c2), m_run, l_run, o);
-  __syncthreads();  // every wave has read K tile 0 before its buffer is refilled
+  barrier_after<0>();  // every wave has read K tile 0 before its buffer is refilled
 
-  // ---- steady state.  Step t (tile t+1 exists):
-  //   phase 1: QK^T MFMAs of tile t+1, interleaved with the exp2 / bf16 / sum
-  //            work of tile t (independent VALU that runs under the MFMAs);
-  //   phase 2: PV MFMAs of tile t, interleaved with the row maximum of tile t+1;
-  //   then the staged K tile t+2 and V tile t+1 go to the free LDS buffers,
-  //   one barrier, and the reference update for tile t+1 (rarely taken).
+  // ---- steady state.  Step t (tile t+1 exists), in fixed instruction order
+  // (sched_barrier fences between bundles keep the compiler from regrouping):
+  //   phase 1: QK^T MFMAs of tile t+1 (K operands read two chunks ahead),
+  //            each followed by exp2 / bf16 / sum work for keys 0..31 of tile t;
+  //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead); the first
+  //            eight carry the exp2 work for keys 32..63 (needed from the ninth
+  //            MFMA on), the next four the row maximum of tile t+1;
+  //   then the requests for K tile t+3 and V tile t+2, one barrier and the
+  //   reference update.  K tile t+1 and V tile t were requested two steps
+  //   earlier (or in the prologue) and ordered by the previous barrier.
   auto step = [&](auto last, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     constexpr bool kLast = decltype(last)::value;  // tile t+1 is the last tile
-    KStage ks;
-    VStage vs;
-    if constexpr (!kLast) {
-      load_k(t + 2, ks);
-      load_v(t + 1, vs);
-    } else {
-      load_v_last(t + 1, vs);
-    }
-    const uint16_t* kt = &sK[(t + 1) & 1][0];
-    const uint16_t* vt = &sV[t & 1][0];
+    const Bases bs = bases((t + 1) % NSTAGE, t % NSTAGE);
+    bf16x8 kf[4];
+    kf[0] = k_frag(bs, 0, 0);
+    kf[1] = k_frag(bs, 1, 0);
+    kf[2] = k_frag(bs, 0, 1);
+    kf[3] = k_frag(bs, 1, 1);
 #pragma unroll
     for (int v = 0; v < 16; ++v) { nxt[0][v] = 0.f; nxt[1][v] = 0.f; }
     bf16x8 pb[4];
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, 0, kc), qf[kc], nxt[0], 0, 0, 0);
-      exp_pair(cur, 4 * kc);
-      nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(kt, 1, kc), qf[kc], nxt[1], 0, 0, 0);
-      exp_pair(cur, 4 * kc + 2);
-      if (kc & 1) pb[kc >> 1] = pack_p(cur, kc >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int sl0 = 2 * (kc & 1);
+      nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0], qf[kc], nxt[0], 0, 0, 0);
+      exp_pair(cur, 2 * kc);  // keys 0..31 of tile t (score registers 0..15 of cur[0])
+      nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0 + 1], qf[kc], nxt[1], 0, 0, 0);
+      if (kc == 3) pb[0] = pack_p(cur, 0);
+      if (kc == 7) pb[1] = pack_p(cur, 1);
+      if (kc + 2 < 8) {
+        kf[sl0] = k_frag(bs, 0, kc + 2);
+        kf[sl0 + 1] = k_frag(bs, 1, kc + 2);
+      }
     }
-    HV_SCHED_GROUP(kSchedVMEMRead, 4, 0);
-    HV_SCHED_GROUP(kSchedDSRead, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      HV_SCHED_GROUP(kSchedMFMA, 1, 0);
-      HV_SCHED_GROUP(kSchedVALU, 6, 0);
-      HV_SCHED_GROUP(kSchedDSRead, 1, 0);
-      HV_SCHED_GROUP(kSchedMFMA, 1, 0);
-      HV_SCHED_GROUP(kSchedVALU, 6, 0);
-      HV_SCHED_GROUP(kSchedDSRead, 1, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (kLast) mask_tile(nxt[0], nxt[1], Lk - (t + 1) * BN, hh);
 
+    bf16x8 vf[2];
+    vf[0] = v_frag(bs, 0, 0);
+    vf[1] = v_frag(bs, 1, 0);
+    float part[4];
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int mm = i >> 2, dt = i & 3;
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 1], pb[mm], o[dt], 0, 0, 0);
+      if (i + 2 < 16) vf[i & 1] = v_frag(bs, (i + 2) & 3, (i + 2) >> 2);
+      if (i < 8) {  // keys 32..63 of tile t, ready before PV chunks 2 and 3
+        exp_pair(cur, 16 + 2 * i);
+        if (i == 3) pb[2] = pack_p(cur, 2);
+        if (i == 7) pb[3] = pack_p(cur, 3);
+      }
+      if (i >= 8 && i < 12) {  // row maximum of tile t+1, in four slices
+        const int j = i - 8;
+        float m = fmaxf(nxt[j >> 1][8 * (j & 1)], nxt[j >> 1][8 * (j & 1) + 1]);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vt, dt, mm), pb[mm], o[dt], 0, 0, 0);
-    const float mx = tile_max(nxt[0], nxt[1], c2);
-    if constexpr (!kLast) store_k(t & 1, ks);
-    store_v((t + 1) & 1, vs);
-    HV_SCHED_GROUP(kSchedDSRead, 4, 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      HV_SCHED_GROUP(kSchedMFMA, 1, 1);
-      HV_SCHED_GROUP(kSchedDSRead, 1, 1);
+        for (int v = 2; v < 8; ++v) m = fmaxf(m, nxt[j >> 1][8 * (j & 1) + v]);
+        part[j] = m;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      HV_SCHED_GROUP(kSchedMFMA, 1, 1);
-      HV_SCHED_GROUP(kSchedVALU, 3, 1);
-      HV_SCHED_GROUP(kSchedDSRead, 1, 1);
-    }
-    HV_SCHED_GROUP(kSchedDSWrite, 10, 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // Request K tile t+3 and V tile t+2 only now, after the last V read of the
+    // step.  The compiler cannot tell which LDS bytes a transposing read
+    // touches, so it waits for every outstanding global->LDS load before the
+    // first one; placed here, that wait falls on the next step's first V
+    // read, a whole QK^T phase later, by which time these loads have landed.
+    // Both tiles are used two steps later, after the next step's barrier,
+    // which orders every wave's share of them.
+    load_k(k_off(t % NSTAGE), min(t + 3, ntiles - 1));
+    load_v(v_off((t + 2) % NSTAGE), min(t + 2, ntiles - 1));
+    const float mx = max_across_halves(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]))) * c2;
+    barrier_after<4>();  // the 4 loads just issued stay in flight
     update_reference(mx, m_run, l_run, o);
   };
 
@@ -388,7 +435,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 
   // ---- last tile: softmax and PV only
   {
-    const uint16_t* vt = &sV[t & 1][0];
+    const Bases bs = bases(0, t % NSTAGE);
     bf16x8 pb[4];
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
@@ -400,8 +447,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vt, dt, mm), pb[mm], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(bs, dt, mm), pb[mm], o[dt], 0, 0, 0);
   }
+  // no LDS access follows; drain the remaining (dead) tile loads before exit
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
   // ---- epilogue: O / l, round to bf16, store rows that exist
   const float inv = 1.0f / sum_across_halves(l_run);
