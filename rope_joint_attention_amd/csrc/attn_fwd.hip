@@ -60,10 +60,11 @@ constexpr int NW = 8;           // waves per workgroup
 constexpr int QPW = 32;         // query rows per wave
 constexpr int BM = NW * QPW;    // 256 query rows per workgroup
 constexpr int NT = NW * 64;     // 512 threads
-constexpr int NSTAGE = 3;       // K/V tiles resident in LDS
+constexpr int NSTAGE = 4;       // K/V tiles resident in LDS (each)
 constexpr int ROWB = D * 2;     // bytes per K/V row in LDS (no padding; swizzled)
 constexpr int TILEB = BN * ROWB;                 // 16 KB per K or V tile
-constexpr int LDS_BYTES = 2 * NSTAGE * TILEB;    // 96 KB
+constexpr int KAHEAD = 4;       // K tile t+KAHEAD is requested in step t
+constexpr int VAHEAD = 3;       // V tile t+VAHEAD is requested in step t
 constexpr float kRescaleLog2 = 8.0f;
 
 // s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt
@@ -160,7 +161,26 @@ __device__ __forceinline__ void update_reference(float mx, float& m_run, float& 
 }
 
 __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[LDS_BYTES];
+  // One LDS array per stage: with every access naming its array at compile
+  // time, the compiler can tell the tile being loaded from the tiles being
+  // read and does not drain the in-flight global->LDS loads before the
+  // transposing reads (which it must otherwise assume to alias them).
+  __shared__ __attribute__((aligned(1024))) unsigned char sK0[TILEB], sK1[TILEB], sK2[TILEB], sK3[TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char sV0[TILEB], sV1[TILEB], sV2[TILEB], sV3[TILEB];
+  auto kbuf = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return sK0; else if constexpr (S == 1) return sK1;
+    else if constexpr (S == 2) return sK2; else return sK3;
+  };
+  auto vbuf = [&](auto st) -> unsigned char* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return sV0; else if constexpr (S == 1) return sV1;
+    else if constexpr (S == 2) return sV2; else return sV3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -201,34 +221,35 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // ---- global -> LDS tile loads.  A tile is 16 wave instructions of 4 rows
   // (1 KB); wave w issues instructions 2w and 2w+1 of each K and V tile.
   // Lane l of an instruction fills LDS slot l%16 of row 4i + l/16, i.e. it
-  // loads chunk (l%16) ^ (row%16) of that row: the swizzle costs nothing and
-  // the 16 lanes of a row still read its 256 contiguous bytes.
-  const int ld_row0 = 8 * wave + (lane >> 4);        // first instruction's row
-  const int ld_kc0 = (lane & 15) ^ (ld_row0 & 15);   // K chunk landing in slot lane%16
+  // loads the chunk the row's swizzle puts in that slot; the 16 lanes of a row
+  // still read its 256 contiguous bytes.  Byte offsets from the tile's first
+  // row are fixed per lane (32 bits: a tile spans 64 rows), so a full tile
+  // costs no vector arithmetic; only the last, partial tile clamps its rows.
+  const int ld_row0 = 8 * wave + (lane >> 4);
+  const int ld_kc0 = (lane & 15) ^ (ld_row0 & 15);
   const int ld_kc1 = (lane & 15) ^ ((ld_row0 + 4) & 15);
-  const int ld_vc = (lane & 15) ^ ((ld_row0 & 3) << 2);  // V: rows r and r+4 swizzle alike
-  // Row offsets are 32-bit byte offsets from the tile's first row (a tile
-  // spans 64 rows, far below 4 GB); only rows past the valid keys, in the
-  // last tile, get clamped.
+  const int ld_vc = (lane & 15) ^ ((ld_row0 & 3) << 2);  // rows 4 apart swizzle alike
   const uint32_t row_bytes = (uint32_t)(sl * 2);
-  auto load_tile = [&](const uint16_t* g, int buf_off, int tile, int c0, int c1) {
-    const int lim = Lk - 1 - tile * BN;  // last valid row, relative to the tile
-    const uint32_t o0 = (uint32_t)min(ld_row0, lim) * row_bytes + c0 * 16;
-    const uint32_t o1 = (uint32_t)min(ld_row0 + 4, lim) * row_bytes + c1 * 16;
+  const uint32_t lk0 = ld_row0 * row_bytes + ld_kc0 * 16, lk1 = (ld_row0 + 4) * row_bytes + ld_kc1 * 16;
+  const uint32_t lv0 = ld_row0 * row_bytes + ld_vc * 16, lv1 = (ld_row0 + 4) * row_bytes + ld_vc * 16;
+  auto load_tile = [&](const uint16_t* g, unsigned char* buf, int tile, uint32_t o0, uint32_t o1,
+                       int c0, int c1) {
     const unsigned char* tb = (const unsigned char*)(g + (int64_t)tile * BN * sl);
-    HV_LDS void* dst = (HV_LDS void*)(lds + buf_off + wave * 2048);
-    __builtin_amdgcn_global_load_lds(tb + o0, dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(tb + o1, (HV_LDS unsigned char*)dst + 1024, 16, 0, 0);
+    unsigned char* dst = buf + wave * 2048;
+    if (tile * BN + BN > Lk) {  // partial last tile: clamp to the last valid row
+      const int lim = Lk - 1 - tile * BN;
+      o0 = (uint32_t)min(ld_row0, lim) * row_bytes + c0 * 16;
+      o1 = (uint32_t)min(ld_row0 + 4, lim) * row_bytes + c1 * 16;
+    }
+    __builtin_amdgcn_global_load_lds(tb + o0, (HV_LDS void*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(tb + o1, (HV_LDS void*)(dst + 1024), 16, 0, 0);
   };
-  auto load_k = [&](int buf_off, int tile) { load_tile(Kg, buf_off, tile, ld_kc0, ld_kc1); };
-  auto load_v = [&](int buf_off, int tile) { load_tile(Vg, buf_off, tile, ld_vc, ld_vc); };
-  auto k_off = [](int stage) { return stage * TILEB; };
-  auto v_off = [](int stage) { return (NSTAGE + stage) * TILEB; };
+  auto load_k = [&](auto st, int tile) { load_tile(Kg, kbuf(st), tile, lk0, lk1, ld_kc0, ld_kc1); };
+  auto load_v = [&](auto st, int tile) { load_tile(Vg, vbuf(st), tile, lv0, lv1, ld_vc, ld_vc); };
 
-  // Operand addresses.  The swizzle only depends on the row modulo 16, so
-  // moving 16 rows (V key groups) or 32 rows (K halves) is a plain immediate
-  // offset; the lane-dependent XOR is folded into 16 per-lane offsets computed
-  // once.  A step only adds the stage base to them.
+  // Operand offsets inside a tile.  The swizzle only depends on the row modulo
+  // 16, so moving 16 rows (V key groups) or 32 rows (K halves) is a plain
+  // immediate; the lane-dependent XOR is folded into 16 per-lane offsets.
   //
   // K operand (rows half*32 + l32, channel chunk 2kc + hh): one 16-byte read.
   int koff[8];
@@ -252,32 +273,20 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         voff[2 * dt + q] = vswz(tr_key + 8 * q, ch >> 3) + 2 * (ch & 7);
       }
   }
-  // Per-step operand bases: stage base + per-lane offset.  The empty asm makes
-  // each base opaque, so the compiler keeps the 16 bases in registers and
-  // folds the K-half / V-key-group offsets into the ds_read immediates rather
-  // than hoisting every (offset + immediate) sum out of the loop.
-  struct Bases {
-    uint32_t k[8], v[8];
-  };
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(HV_LDS unsigned char*)lds;
-  auto bases = [&](int kstage, int vstage) {
-    Bases bs;
+  // Re-declared opaque once per step, so the compiler keeps the 16 offsets in
+  // registers and folds array base + stage-free immediates into the ds_read
+  // offset fields, instead of hoisting every (offset + immediate) sum.
+  auto refresh_offsets = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      bs.k[i] = lds_base + k_off(kstage) + koff[i];
-      bs.v[i] = lds_base + v_off(vstage) + voff[i];
-      asm volatile("" : "+v"(bs.k[i]), "+v"(bs.v[i]));
-    }
-    return bs;
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(koff[i]), "+v"(voff[i]));
   };
-  auto k_frag = [&](const Bases& bs, int half, int kc) {
-    return *(const HV_LDS bf16x8*)(uintptr_t)(bs.k[kc] + half * 32 * ROWB);
+  auto k_frag = [&](auto st, int half, int kc) {
+    return *reinterpret_cast<const bf16x8*>(kbuf(st) + koff[kc] + half * 32 * ROWB);
   };
-  auto v_frag = [&](const Bases& bs, int dt, int mm) {
-    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (HV_LDS i16x4*)(uintptr_t)(bs.v[2 * dt] + mm * 16 * ROWB));
-    const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (HV_LDS i16x4*)(uintptr_t)(bs.v[2 * dt + 1] + mm * 16 * ROWB));
+  auto v_frag = [&](auto st, int dt, int mm) {
+    unsigned char* vb = vbuf(st);
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(vb + voff[2 * dt] + mm * 16 * ROWB));
+    const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(vb + voff[2 * dt + 1] + mm * 16 * ROWB));
     const u32x4 w = {__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1],
                      __builtin_bit_cast(u32x2, c)[0], __builtin_bit_cast(u32x2, c)[1]};
     return __builtin_bit_cast(bf16x8, w);
@@ -293,6 +302,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const float c2 = p.scale_log2;
   const int ntiles = (Lk + BN - 1) / BN;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
   // exp2 of scores e0, e0+1 of tile registers s (in place)
   auto exp_pair = [&](f32x16 (&s)[2], int e0) {
@@ -318,75 +328,84 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     return __builtin_bit_cast(bf16x8, v);
   };
 
-  // ---- prologue: K tiles 0..2 and V tiles 0..1 requested; scores of tile 0
-  load_k(k_off(0), 0);
-  load_k(k_off(1), min(1, ntiles - 1));
-  load_k(k_off(2), min(2, ntiles - 1));
-  load_v(v_off(0), 0);
-  load_v(v_off(1), min(1, ntiles - 1));
+  // ---- prologue: K tiles 0..3 and V tiles 0..2 requested; scores of tile 0
+  load_k(I0{}, 0);
+  load_k(I1{}, min(1, ntiles - 1));
+  load_k(I2{}, min(2, ntiles - 1));
+  load_k(I3{}, min(3, ntiles - 1));
+  load_v(I0{}, 0);
+  load_v(I1{}, min(1, ntiles - 1));
+  load_v(I2{}, min(2, ntiles - 1));
   barrier_after<0>();
   f32x16 sa[2], sb[2];
-  const Bases b0 = bases(0, 0);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) { sa[0][v] = 0.f; sa[1][v] = 0.f; }
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
-    sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(b0, 0, kc), qf[kc], sa[0], 0, 0, 0);
-    sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(b0, 1, kc), qf[kc], sa[1], 0, 0, 0);
+    sa[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(I0{}, 0, kc), qf[kc], kc ? sa[0] : zero16, 0, 0, 0);
+    sa[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(I0{}, 1, kc), qf[kc], kc ? sa[1] : zero16, 0, 0, 0);
   }
   if (ntiles == 1) mask_tile(sa[0], sa[1], Lk, hh);
   update_reference(tile_max(sa[0], sa[1], c2), m_run, l_run, o);
+  // K operands of the first step (tile 1) are read before its barrier
+  bf16x8 kf[4];
+  kf[0] = k_frag(I1{}, 0, 0);
+  kf[1] = k_frag(I1{}, 1, 0);
+  kf[2] = k_frag(I1{}, 0, 1);
+  kf[3] = k_frag(I1{}, 1, 1);
   barrier_after<0>();  // every wave has read K tile 0 before its buffer is refilled
 
-  // ---- steady state.  Step t (tile t+1 exists), in fixed instruction order
-  // (sched_barrier fences between bundles keep the compiler from regrouping):
-  //   phase 1: QK^T MFMAs of tile t+1 (K operands read two chunks ahead),
-  //            each followed by exp2 / bf16 / sum work for keys 0..31 of tile t;
+  // ---- steady state.  Step t (tile t+1 exists; U = t % 4 at compile time),
+  // in fixed instruction order (sched_barrier fences between bundles keep the
+  // compiler from regrouping):
+  //   phase 1: QK^T MFMAs of tile t+1 (its first K operands were read before
+  //            the previous barrier, the rest two chunks ahead), each followed
+  //            by exp2 / bf16 / sum work for keys 0..31 of tile t;
   //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead); the first
-  //            eight carry the exp2 work for keys 32..63 (needed from the ninth
-  //            MFMA on), the next four the row maximum of tile t+1;
-  //   then the requests for K tile t+3 and V tile t+2, one barrier and the
-  //   reference update.  K tile t+1 and V tile t were requested two steps
-  //   earlier (or in the prologue) and ordered by the previous barrier.
-  auto step = [&](auto last, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    constexpr bool kLast = decltype(last)::value;  // tile t+1 is the last tile
-    const Bases bs = bases((t + 1) % NSTAGE, t % NSTAGE);
-    bf16x8 kf[4];
-    kf[0] = k_frag(bs, 0, 0);
-    kf[1] = k_frag(bs, 1, 0);
-    kf[2] = k_frag(bs, 0, 1);
-    kf[3] = k_frag(bs, 1, 1);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { nxt[0][v] = 0.f; nxt[1][v] = 0.f; }
+  //            eight carry the exp2 work for keys 32..63, the next four the row
+  //            maximum of tile t+1;
+  //   then requests for K tile t+4 and V tile t+3, the first K operands of
+  //   tile t+2 for the next step, one barrier and the reference update.
+  // K tile t+1 and V tile t were requested three steps earlier (or in the
+  // prologue); every barrier waits for the loads of the step before it, so a
+  // tile is complete and visible from the barrier that follows its request
+  // step by one.
+  auto step = [&](auto u, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr int U = decltype(u)::value;
+    using KS = std::integral_constant<int, (U + 1) % NSTAGE>;   // K tile t+1
+    using VS = std::integral_constant<int, U>;                  // V tile t
+    using KN = std::integral_constant<int, (U + 2) % NSTAGE>;   // K tile t+2
+    using KL = std::integral_constant<int, U>;                  // K tile t+4 goes here
+    using VL = std::integral_constant<int, (U + 3) % NSTAGE>;   // V tile t+3 goes here
+    refresh_offsets();
     bf16x8 pb[4];
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       __builtin_amdgcn_sched_barrier(0);
       const int sl0 = 2 * (kc & 1);
-      nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0], qf[kc], nxt[0], 0, 0, 0);
+      nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0], qf[kc], kc ? nxt[0] : zero16, 0, 0, 0);
       exp_pair(cur, 2 * kc);  // keys 0..31 of tile t (score registers 0..15 of cur[0])
-      nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0 + 1], qf[kc], nxt[1], 0, 0, 0);
+      nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0 + 1], qf[kc], kc ? nxt[1] : zero16, 0, 0, 0);
       if (kc == 3) pb[0] = pack_p(cur, 0);
       if (kc == 7) pb[1] = pack_p(cur, 1);
       if (kc + 2 < 8) {
-        kf[sl0] = k_frag(bs, 0, kc + 2);
-        kf[sl0 + 1] = k_frag(bs, 1, kc + 2);
+        kf[sl0] = k_frag(KS{}, 0, kc + 2);
+        kf[sl0 + 1] = k_frag(KS{}, 1, kc + 2);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    if constexpr (kLast) mask_tile(nxt[0], nxt[1], Lk - (t + 1) * BN, hh);
+    // keep phase-1 results where they are computed (not sunk past the branch)
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]));
+    if (t + 2 == ntiles) mask_tile(nxt[0], nxt[1], Lk - (t + 1) * BN, hh);
 
     bf16x8 vf[2];
-    vf[0] = v_frag(bs, 0, 0);
-    vf[1] = v_frag(bs, 1, 0);
+    vf[0] = v_frag(VS{}, 0, 0);
+    vf[1] = v_frag(VS{}, 1, 0);
     float part[4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       const int mm = i >> 2, dt = i & 3;
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 1], pb[mm], o[dt], 0, 0, 0);
-      if (i + 2 < 16) vf[i & 1] = v_frag(bs, (i + 2) & 3, (i + 2) >> 2);
+      if (i + 2 < 16) vf[i & 1] = v_frag(VS{}, (i + 2) & 3, (i + 2) >> 2);
       if (i < 8) {  // keys 32..63 of tile t, ready before PV chunks 2 and 3
         exp_pair(cur, 16 + 2 * i);
         if (i == 3) pb[2] = pack_p(cur, 2);
@@ -401,41 +420,33 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // Request K tile t+3 and V tile t+2 only now, after the last V read of the
-    // step.  The compiler cannot tell which LDS bytes a transposing read
-    // touches, so it waits for every outstanding global->LDS load before the
-    // first one; placed here, that wait falls on the next step's first V
-    // read, a whole QK^T phase later, by which time these loads have landed.
-    // Both tiles are used two steps later, after the next step's barrier,
-    // which orders every wave's share of them.
-    load_k(k_off(t % NSTAGE), min(t + 3, ntiles - 1));
-    load_v(v_off((t + 2) % NSTAGE), min(t + 2, ntiles - 1));
+    kf[0] = k_frag(KN{}, 0, 0);
+    kf[1] = k_frag(KN{}, 1, 0);
+    kf[2] = k_frag(KN{}, 0, 1);
+    kf[3] = k_frag(KN{}, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(KL{}, min(t + KAHEAD, ntiles - 1));
+    load_v(VL{}, min(t + VAHEAD, ntiles - 1));
     const float mx = max_across_halves(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]))) * c2;
     barrier_after<4>();  // the 4 loads just issued stay in flight
     update_reference(mx, m_run, l_run, o);
   };
 
-  using Plain = std::integral_constant<bool, false>;
-  using Last = std::integral_constant<bool, true>;
-  int t = 0;
-  for (; t + 3 < ntiles; t += 2) {
-    step(Plain{}, t, sa, sb);
-    step(Plain{}, t + 1, sb, sa);
+  const int last = ntiles - 1;  // steps run for t = 0 .. last-1
+  for (int t = 0; t < last; t += 4) {
+    step(I0{}, t, sa, sb);
+    if (t + 1 < last) step(I1{}, t + 1, sb, sa);
+    if (t + 2 < last) step(I2{}, t + 2, sa, sb);
+    if (t + 3 < last) step(I3{}, t + 3, sb, sa);
   }
-  if (t + 2 < ntiles) {
-    step(Plain{}, t, sa, sb);
-    step(Last{}, t + 1, sb, sa);
-    t += 2;
-  } else if (t + 1 < ntiles) {
-    step(Last{}, t, sa, sb);
-    ++t;
+  // scores of the last tile: sa if it is tile 0, 2, 4, ...
+  if (last & 1) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) { sa[0][v] = sb[0][v]; sa[1][v] = sb[1][v]; }
   }
 
   // ---- last tile: softmax and PV only
   {
-    const Bases bs = bases(0, t % NSTAGE);
     bf16x8 pb[4];
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
@@ -443,11 +454,19 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       exp_pair(sa, 4 * kc + 2);
       if (kc & 1) pb[kc >> 1] = pack_p(sa, kc >> 1);
     }
+    auto final_pv = [&](auto st) {
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
+      for (int mm = 0; mm < 4; ++mm)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(bs, dt, mm), pb[mm], o[dt], 0, 0, 0);
+        for (int dt = 0; dt < 4; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(st, dt, mm), pb[mm], o[dt], 0, 0, 0);
+    };
+    switch (last % NSTAGE) {
+      case 0: final_pv(I0{}); break;
+      case 1: final_pv(I1{}); break;
+      case 2: final_pv(I2{}); break;
+      default: final_pv(I3{}); break;
+    }
   }
   // no LDS access follows; drain the remaining (dead) tile loads before exit
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
