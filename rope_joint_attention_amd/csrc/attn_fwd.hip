@@ -433,12 +433,16 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   };
 
   const int last = ntiles - 1;  // steps run for t = 0 .. last-1
-  for (int t = 0; t < last; t += 4) {
+  int t = 0;
+  for (; t + 4 <= last; t += 4) {  // branch-free body: four full steps
     step(I0{}, t, sa, sb);
-    if (t + 1 < last) step(I1{}, t + 1, sb, sa);
-    if (t + 2 < last) step(I2{}, t + 2, sa, sb);
-    if (t + 3 < last) step(I3{}, t + 3, sb, sa);
+    step(I1{}, t + 1, sb, sa);
+    step(I2{}, t + 2, sa, sb);
+    step(I3{}, t + 3, sb, sa);
   }
+  if (t < last) step(I0{}, t, sa, sb);
+  if (t + 1 < last) step(I1{}, t + 1, sb, sa);
+  if (t + 2 < last) step(I2{}, t + 2, sa, sb);
   // scores of the last tile: sa if it is tile 0, 2, 4, ...
   if (last & 1) {
 #pragma unroll
