@@ -43,8 +43,13 @@ def attn_flops(batch: int, seq_len: int, lk) -> float:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernel's code with comments and blank lines removed,
+    so that a comment edit does not invalidate recorded counters."""
     p = os.path.join(ROOT, "rope_joint_attention_amd", "csrc", "attn_fwd.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    text = re.sub(r"/\*.*?\*/", "", open(p).read(), flags=re.S)
+    code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in code if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def recorded_traffic(workload: str):
@@ -99,7 +104,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()

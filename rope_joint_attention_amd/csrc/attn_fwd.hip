@@ -12,8 +12,9 @@
 //     waves per SIMD;
 //   * K and V tiles of 64 keys reach LDS by direct global->LDS loads
 //     (global_load_lds_dwordx4: no registers, fully coalesced 1 KB per wave
-//     instruction) into three LDS stages, each tile requested two steps
-//     before it is used;
+//     instruction) into four LDS stages each for K and V; K tile t+4 and
+//     V tile t+3 are requested during step t, and each wave waits only for
+//     its own oldest loads (s_waitcnt vmcnt) before the step's one barrier;
 //   * workgroup ids are remapped so that consecutive query blocks of one
 //     (batch, head) run on the same XCD and share its L2 for K/V.
 //
