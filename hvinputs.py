@@ -8,6 +8,7 @@ no token-grid formula, no rotary embedding, no attention.  It only knows
 * how to draw Q, K, V ~ N(0, 1) from NumPy's PCG64 and round them to bfloat16
   bit patterns (round-to-nearest-even, done with integer arithmetic);
 * how to widen bfloat16 bit patterns back to float32 / float64 (exact);
+* how to draw synthetic RMSNorm weights (near one) for the QK-norm prologue;
 * a deterministic query-row sampler used where the full fp64 oracle would be
   too slow.
 
@@ -150,6 +151,22 @@ def draw_qkv(batch: int, seq_len: int, seed: int,
             for s, n, f in futs:
                 flat[s:s + n] = f.result()
             out[name] = flat.reshape(shape)
+    return out
+
+
+def draw_gamma(seed: int, head_dim: int = HEAD_DIM, spread: float = 0.25) -> Dict[str, np.ndarray]:
+    """Synthetic RMSNorm weights as bfloat16 bit patterns, one [head_dim]
+    vector each for video Q, video K, text Q and text K.
+
+    Values are 1 + spread * N(0, 1) (float32 from
+    PCG64(SeedSequence(seed, spawn_key=(3 + i,))) for vector i), rounded to
+    bfloat16, standing in for trained weights that stay near one.
+    """
+    out = {}
+    for i, name in enumerate(("q_video", "k_video", "q_text", "k_text")):
+        ss = np.random.SeedSequence(entropy=seed, spawn_key=(3 + i,))
+        x = np.random.Generator(np.random.PCG64(ss)).standard_normal(size=head_dim, dtype=np.float32)
+        out[name] = f32_to_bf16_bits(np.float32(1.0) + np.float32(spread) * x)
     return out
 
 

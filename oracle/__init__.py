@@ -17,7 +17,10 @@ Each function restates, in NumPy float64, what the HunyuanVideo notes page
                       with padded text keys left out (section 3.1 keeps at
                       most 256 prompt tokens; section 5.2 names the valid
                       text length);
-* ``hot_path``        the three in sequence.
+* ``rms_norm_heads``  section 5.4, per-head RMSNorm of Q and K;
+* ``qk_norm_rope3d``  RMSNorm (video / text gamma, section 5.2) followed by the
+                      3D RoPE of section 5.5;
+* ``hot_path``        token grid, RoPE and attention in sequence.
 
 Nothing here is blocked, fused or reordered beyond the formulas: the matrix
 products use NumPy's matmul as a library primitive, and query rows are
@@ -26,7 +29,9 @@ processed in independent chunks only to bound memory.
 Pins (tests/test_oracle_*.py): printed token counts, closed-form rotation
 angles, norm and relative-position invariants, the complex-number form of
 RoPE, uniform/one-key/two-key closed forms, permutation and shift
-invariance, masking with poisoned values, and a pure-Python brute force.
+invariance, masking with poisoned values, a pure-Python brute force, and for
+the RMSNorm unit output RMS, scale invariance, an epsilon closed form, head and
+channel isolation and the per-pair magnitudes that fix its order against RoPE.
 """
 from .hv_oracle import (  # noqa: F401
     HEADS,
@@ -37,6 +42,8 @@ from .hv_oracle import (  # noqa: F401
     rope_frequencies,
     video_coordinates,
     apply_rope3d,
+    rms_norm_heads,
+    qk_norm_rope3d,
     joint_attention,
     hot_path,
 )

@@ -118,6 +118,40 @@ def apply_rope3d(x: np.ndarray, token_index: np.ndarray, grid: OracleGrid,
     return x
 
 
+def rms_norm_heads(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """Per-head RMSNorm, float64 (notes page section 5.4).
+
+    Each head vector x (the last axis, d = 128 channels) becomes
+        gamma * x / sqrt(mean_j(x_j^2) + eps).
+    ``gamma`` broadcasts against ``x`` (a [128] vector, or one per row).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mean_sq = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(gamma, dtype=np.float64) * (x / np.sqrt(mean_sq + eps))
+
+
+def qk_norm_rope3d(x: np.ndarray, token_index: np.ndarray, grid: OracleGrid, theta: float,
+                   gamma_video: np.ndarray, gamma_text: Optional[np.ndarray],
+                   eps: float) -> np.ndarray:
+    """QK-norm prologue of the attention: per-head RMSNorm, then 3D RoPE.
+
+    Section 5.4 normalises every head of Q and K with an RMSNorm; section 5.2
+    keeps separate parameters for the video and text streams in the
+    double-stream blocks, so video rows use ``gamma_video`` and text rows
+    ``gamma_text`` (the same vector when it is None, as in the single-stream
+    blocks of section 5.3).  Section 5.5 then rotates the video rows.
+    ``x``: float64 [..., R, HEADS, HEAD_DIM] holding the rows listed in
+    ``token_index``.  Returns a float64 array of the same shape.
+    """
+    token_index = np.asarray(token_index, dtype=np.int64)
+    gv = np.asarray(gamma_video, dtype=np.float64)
+    gt = gv if gamma_text is None else np.asarray(gamma_text, dtype=np.float64)
+    is_video = token_index < grid.n_video
+    g = np.where(is_video[:, None], gv[None, :], gt[None, :])[:, None, :]   # [R, 1, D]
+    y = rms_norm_heads(x, g, eps)
+    return apply_rope3d(y, token_index, grid, theta)
+
+
 def joint_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_video: int,
                     valid: Sequence[int], scale: Optional[float] = None,
                     rows: Optional[np.ndarray] = None,
