@@ -13,7 +13,9 @@ Printed: ONE JSON line (stdout) with the whole-step throughput in attention
 TFLOP/s (algorithmic FLOPs 4*heads*head_dim*sum_b L*Lk_b over the step time),
 per-kernel times from HIP events on the launch stream, the attention
 kernel's MFMA roofline fraction, and the fp64 oracle timed on a bounded
-sample of the same workload on the host cores.
+sample of the same workload on the host cores.  The QK-norm + RoPE prologue
+(hv_qk_norm_rope3d_apply, all rows of q and k) is timed separately on the
+same resident tensors and reported beside the step (qknorm_rope_*).
 """
 from __future__ import annotations
 
@@ -175,6 +177,26 @@ def main() -> int:
     attn_ms = [e[1].elapsed_time(e[2]) for e in events]
     progress(f"timed {args.steps} steps in {wall:.2f} s")
 
+    # The QK-norm + RoPE prologue (an alternative to the RoPE step that also
+    # normalises every row): timed on its own, on the same resident q and k.
+    gam = {n: to_dev(b) for n, b in hvinputs.draw_gamma(wl.seed).items()}
+    g0 = hv.hv_token_grid(wl.frames, wl.height, wl.width)
+
+    def prologue():
+        hv.hv_qk_norm_rope3d_apply(q, k, g0, wl.theta, gam["q_video"], gam["k_video"],
+                                   gam["q_text"], gam["k_text"], 1e-6)
+
+    for _ in range(2):
+        prologue()
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        pev[i][0].record(stream)
+        prologue()
+        pev[i][1].record(stream)
+    torch.cuda.synchronize()
+    qkn_ms = [e[0].elapsed_time(e[1]) for e in pev]
+    progress(f"timed {args.steps} QK-norm + RoPE prologue calls")
+
     if args.copy_ref_mib > 0:
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -192,6 +214,9 @@ def main() -> int:
     rope_bytes = 4.0 * wl.batch * grid.n_video * HEADS * HEAD_DIM * 2
     rope_gbps = rope_bytes / (rope_avg / 1000.0) / 1e9
     traffic = recorded_traffic(name)
+    qkn_avg = float(np.mean(qkn_ms))
+    qkn_bytes = 4.0 * wl.batch * L * HEADS * HEAD_DIM * 2
+    qkn_gbps = qkn_bytes / (qkn_avg / 1000.0) / 1e9
 
     result = {
         "metric": METRIC,
@@ -217,6 +242,9 @@ def main() -> int:
         "rope_GBps": round(rope_gbps, 1),
         "rope_pct_hbm_peak": round(100.0 * rope_gbps / PEAK_HBM_GBPS, 2),
         "attn_flops_per_call": flops,
+        "qknorm_rope_ms_per_call": round(qkn_avg, 4),
+        "qknorm_rope_GBps": round(qkn_gbps, 1),
+        "qknorm_rope_pct_hbm_peak": round(100.0 * qkn_gbps / PEAK_HBM_GBPS, 2),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),

@@ -9,6 +9,8 @@
  *                 (16, 56, 56)); the technical-report summary page
  *                 (zhao9797.github.io, "hunyuan-video"), Table 2 paragraph,
  *                 gives the same split;
+ *   - QK norm:    section 5.4 (per-head RMSNorm of Q and K), section 5.2
+ *                 (separate video / text weights in double-stream blocks);
  *   - attention:  section 5.2 (joint softmax attention over [video; text],
  *                 scale 1/sqrt(128)); section 3.1 (at most 256 text tokens);
  *                 section 5.1 (24 heads x 128).
@@ -102,6 +104,32 @@ int hv_token_grid(int32_t frames, int32_t height, int32_t width, hv_grid* out);
  * alignment, overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
 int hv_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
                     const hv_grid* grid, float theta, void* stream);
+
+/* hv_qk_norm_rope3d_apply: the QK-norm prologue of the attention, in place:
+ * per-head RMSNorm of every row of q and k (notes page section 5.4:
+ * y = gamma * x / sqrt(mean_j x_j^2 + eps) over the 128 channels of a head),
+ * then the rotation of hv_rope3d_apply on the video rows (section 5.5).
+ * Video rows (n < grid->n_video) use gamma_q / gamma_k; text rows use
+ * gamma_q_text / gamma_k_text (section 5.2: the double-stream blocks keep
+ * separate weights per stream); a NULL text weight means the video weight
+ * (the shared weights of the single-stream blocks, section 5.3).  All
+ * seq_len rows are normalised, padded text rows included.  Math is fp32;
+ * each result is rounded to bf16 (nearest even) once, after the rotation.
+ *   q, k      device pointers, layout *layout; may not overlap each other
+ *   grid      from hv_token_grid; layout->seq_len >= grid->n_video
+ *   theta     rotary base, finite and > 0
+ *   gamma_*   device pointers to 128 bf16 weights, 16-byte aligned, outside
+ *             q and k (they may alias one another)
+ *   eps       finite and >= 0 (with eps == 0 an all-zero head gives NaN, as
+ *             the formula does)
+ * Errors: HV_ERR_INVALID_ARG (NULL q/k/gamma_q/gamma_k, inconsistent grid,
+ * theta <= 0, eps < 0 or not finite, alignment, overlap), HV_ERR_UNSUPPORTED,
+ * HV_ERR_HIP. */
+int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
+                            const hv_grid* grid, float theta,
+                            const hv_bf16* gamma_q, const hv_bf16* gamma_k,
+                            const hv_bf16* gamma_q_text, const hv_bf16* gamma_k_text,
+                            float eps, void* stream);
 
 /* hv_joint_attention_fwd: out = softmax(scale * Q K^T) V per (batch, head)
  * over the joint [video; text] sequence (notes page section 5.2).

@@ -8,6 +8,8 @@ not built, every call raises (there is no fallback).
 
     hv_token_grid(frames, height, width) -> HvGrid
     hv_rope3d_apply(q, k, grid, theta)          # in place on video rows
+    hv_qk_norm_rope3d_apply(q, k, grid, theta, gamma_q, gamma_k,
+                            gamma_q_text=None, gamma_k_text=None, eps=1e-6)
     hv_joint_attention_fwd(q, k, v, text_valid_len, n_video, out=None,
                            softmax_scale=None) -> out
 """
@@ -19,7 +21,7 @@ from typing import Optional, Sequence
 
 __all__ = [
     "HV_HEADS", "HV_HEAD_DIM", "HV_MAX_BATCH", "HvError", "HvGrid",
-    "hv_token_grid", "hv_rope3d_apply", "hv_joint_attention_fwd",
+    "hv_token_grid", "hv_rope3d_apply", "hv_qk_norm_rope3d_apply", "hv_joint_attention_fwd",
     "hv_status_string", "library_path", "load_library",
 ]
 
@@ -91,6 +93,11 @@ def load_library():
     lib.hv_rope3d_apply.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Layout),
                                     ctypes.POINTER(_Grid), ctypes.c_float, ctypes.c_void_p]
     lib.hv_rope3d_apply.restype = ctypes.c_int
+    lib.hv_qk_norm_rope3d_apply.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Layout),
+                                            ctypes.POINTER(_Grid), ctypes.c_float,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
+    lib.hv_qk_norm_rope3d_apply.restype = ctypes.c_int
     lib.hv_joint_attention_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p,
                                            ctypes.POINTER(_Layout), ctypes.c_int64, ctypes.c_float,
@@ -154,6 +161,37 @@ def hv_rope3d_apply(q, k, grid: HvGrid, theta: float = 10000.0) -> None:
                                         ctypes.byref(g), float(theta), _stream_of(q))
     if st != HV_OK:
         raise HvError(st, "hv_rope3d_apply")
+
+
+def _weight_ptr(g, what: str, device) -> Optional[int]:
+    import torch
+
+    if g is None:
+        return None
+    if g.dtype != torch.bfloat16 or g.device != device:
+        raise TypeError(f"{what} must be a bfloat16 tensor on {device}")
+    if g.dim() != 1 or g.shape[0] != HV_HEAD_DIM or g.stride(0) != 1:
+        raise ValueError(f"{what} must be a contiguous [{HV_HEAD_DIM}] vector, got {tuple(g.shape)}")
+    return g.data_ptr()
+
+
+def hv_qk_norm_rope3d_apply(q, k, grid: HvGrid, theta: float, gamma_q, gamma_k,
+                            gamma_q_text=None, gamma_k_text=None, eps: float = 1e-6) -> None:
+    """Per-head RMSNorm of every row of q and k, then 3D RoPE of the video rows,
+    in place (see hvattn.h).  gamma_* are bfloat16 [128] device vectors; the text
+    weights default to the video ones."""
+    lay = _layout_of(q, "q")
+    if not _same_layout(lay, _layout_of(k, "k")):
+        raise ValueError("q and k must share shape and strides")
+    g = grid._c()
+    ptrs = [_weight_ptr(w, n, q.device) for w, n in ((gamma_q, "gamma_q"), (gamma_k, "gamma_k"),
+                                                     (gamma_q_text, "gamma_q_text"),
+                                                     (gamma_k_text, "gamma_k_text"))]
+    st = load_library().hv_qk_norm_rope3d_apply(q.data_ptr(), k.data_ptr(), ctypes.byref(lay),
+                                                ctypes.byref(g), float(theta), *ptrs, float(eps),
+                                                _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_qk_norm_rope3d_apply")
 
 
 def hv_joint_attention_fwd(q, k, v, text_valid_len: Optional[Sequence[int]], n_video: int,

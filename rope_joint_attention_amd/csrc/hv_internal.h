@@ -29,6 +29,31 @@ struct RopeParams {
 
 hipError_t launch_rope3d(const RopeParams& p, hipStream_t stream);
 
+// ---- QK-norm + 3D RoPE prologue ---------------------------------------------
+// Per-head RMSNorm of every row of q and k (video rows with gamma_q/gamma_k,
+// text rows with gamma_q_text/gamma_k_text, which the host sets to the video
+// weights when the caller passes none), then the rotation of RopeParams on
+// the video rows.
+struct QkNormParams {
+  uint16_t* q;
+  uint16_t* k;
+  const uint16_t* gamma_q;
+  const uint16_t* gamma_k;
+  const uint16_t* gamma_q_text;
+  const uint16_t* gamma_k_text;
+  int64_t stride_b;  // elements
+  int64_t stride_l;  // elements
+  int32_t batch;
+  int32_t seq_len;
+  int32_t n_video;
+  int32_t gh;        // token grid height
+  int32_t gw;        // token grid width
+  float eps;
+  float freq[64];    // as in RopeParams
+};
+
+hipError_t launch_qknorm_rope3d(const QkNormParams& p, hipStream_t stream);
+
 // ---- joint attention forward ----------------------------------------------
 struct AttnParams {
   const uint16_t* q;

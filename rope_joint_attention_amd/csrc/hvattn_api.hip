@@ -60,6 +60,17 @@ int check_grid(const hv_grid* g) {
   return HV_OK;
 }
 
+// The 64 rotation frequencies of a head, pair p = 0..63: pairs 0..7 form the
+// time block (width 16), 8..35 height (56), 36..63 width (56);
+// freq = theta^(-2j/width) with j the pair's index inside its block.
+void rope_frequencies(float theta, float* freq) {
+  const int widths[3] = {16, 56, 56};
+  int pair = 0;
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < widths[a] / 2; ++j)
+      freq[pair++] = (float)pow((double)theta, -2.0 * j / widths[a]);
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,13 +132,61 @@ int hv_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout, const hv_gr
   p.n_video = (int32_t)grid->n_video;
   p.gh = grid->gh;
   p.gw = grid->gw;
-  // (offset, width) of the time, height and width blocks: (0,16), (16,56), (72,56)
-  const int widths[3] = {16, 56, 56};
-  int pair = 0;
-  for (int a = 0; a < 3; ++a)
-    for (int j = 0; j < widths[a] / 2; ++j)
-      p.freq[pair++] = (float)pow((double)theta, -2.0 * j / widths[a]);
+  rope_frequencies(theta, p.freq);
   const hipError_t e = hv::launch_rope3d(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
+int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout, const hv_grid* grid,
+                            float theta, const hv_bf16* gamma_q, const hv_bf16* gamma_k,
+                            const hv_bf16* gamma_q_text, const hv_bf16* gamma_k_text, float eps,
+                            void* stream) {
+  int64_t extent = 0;
+  int st = check_layout(layout, &extent);
+  if (st != HV_OK) return st;
+  st = check_grid(grid);
+  if (st != HV_OK) return st;
+  if (!(theta > 0.f) || !isfinite(theta)) return HV_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return HV_ERR_INVALID_ARG;
+  if (grid->n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
+  if (!q || !k || !gamma_q || !gamma_k) return HV_ERR_INVALID_ARG;
+  if (!gamma_q_text) gamma_q_text = gamma_q;
+  if (!gamma_k_text) gamma_k_text = gamma_k;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(gamma_q) || !aligned16(gamma_k) ||
+      !aligned16(gamma_q_text) || !aligned16(gamma_k_text))
+    return HV_ERR_INVALID_ARG;
+  if (overlap(q, k, layout, extent)) return HV_ERR_INVALID_ARG;
+  // the weights are read while q and k are written: they must lie outside both
+  const uintptr_t gbytes = HV_HEAD_DIM * sizeof(hv_bf16);
+  const uintptr_t tbytes = (uintptr_t)extent * sizeof(hv_bf16);
+  const void* gammas[4] = {gamma_q, gamma_k, gamma_q_text, gamma_k_text};
+  for (const void* g : gammas) {
+    const uintptr_t x = (uintptr_t)g;
+    for (const void* t : {(const void*)q, (const void*)k}) {
+      const uintptr_t y = (uintptr_t)t;
+      if (x < y + tbytes && y < x + gbytes) return HV_ERR_INVALID_ARG;
+    }
+  }
+  if (layout->batch == 0 || layout->seq_len == 0) return HV_OK;
+
+  hv::QkNormParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.gamma_q = gamma_q;
+  p.gamma_k = gamma_k;
+  p.gamma_q_text = gamma_q_text;
+  p.gamma_k_text = gamma_k_text;
+  p.stride_b = layout->stride_b;
+  p.stride_l = layout->stride_l;
+  p.batch = layout->batch;
+  p.seq_len = layout->seq_len;
+  p.n_video = (int32_t)grid->n_video;
+  p.gh = grid->gh;
+  p.gw = grid->gw;
+  p.eps = eps;
+  rope_frequencies(theta, p.freq);
+  const hipError_t e = hv::launch_qknorm_rope3d(p, (hipStream_t)stream);
   return e == hipSuccess ? HV_OK : HV_ERR_HIP;
 }
 

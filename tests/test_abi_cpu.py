@@ -198,3 +198,49 @@ def test_odd_byte_offset_counts_as_aliasing():
     # 16-byte aligned but an odd element offset is impossible; an unaligned
     # pointer is rejected first, by the alignment rule
     assert rope(k=FAKE + 2 * 3072 + 1, lay=lay) == E
+
+
+# ---------------------------------------------------- QK-norm + RoPE prologue
+GQ, GK = FAKE + 4 * SEP, FAKE + 4 * SEP + 256
+
+
+def qknorm(q=FAKE, k=FAKE + SEP, lay=None, g=None, theta=10000.0, gq=GQ, gk=GK, gqt=None, gkt=None,
+           eps=1e-6):
+    lib = hv.load_library()
+    lay = layout() if lay is None else lay
+    g = grid() if g is None else g
+    return lib.hv_qk_norm_rope3d_apply(q, k, ctypes.byref(lay) if lay is not False else None,
+                                       ctypes.byref(g) if g is not False else None, theta,
+                                       gq, gk, gqt, gkt, eps, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(k=0), E), (dict(gq=0), E), (dict(gk=0), E),
+    (dict(lay=False), E), (dict(g=False), E),
+    (dict(q=FAKE + 2), E), (dict(gq=GQ + 8), E), (dict(gk=GK + 2), E),
+    (dict(gqt=GQ + 4 + 512), E), (dict(gkt=GK + 8 + 512), E),
+    (dict(k=FAKE + 3072 * 2), E),                         # k overlaps q
+    (dict(gq=FAKE + 160 * 3072 * 2), E),                  # weight inside q
+    (dict(gk=FAKE + SEP + 299 * 3072 * 2 + 128), E),      # weight inside k's last row
+    (dict(gqt=FAKE + SEP - 128), E),                      # text weight straddles k's start
+    (dict(theta=0.0), E), (dict(theta=float("nan")), E),
+    (dict(eps=-1e-6), E), (dict(eps=float("nan")), E), (dict(eps=float("inf")), E),
+    (dict(lay=layout(heads=16)), U), (dict(lay=layout(dim=64)), U), (dict(lay=layout(batch=65)), U),
+    (dict(lay=layout(batch=-1)), E), (dict(lay=layout(sl=3076)), E),
+    (dict(lay=layout(seq=39)), E),                        # fewer rows than video tokens
+])
+def test_qknorm_validation(kwargs, expect):
+    assert qknorm(**kwargs) == expect
+
+
+def test_qknorm_weights_may_alias_each_other_and_empty_calls_are_noops():
+    # shared weights (text = video, q = k) pass validation; batch 0 launches nothing
+    assert qknorm(gk=GQ, gqt=GQ, gkt=GQ, lay=layout(batch=0)) == hv.HV_OK
+    assert qknorm(lay=layout(seq=0, sb=0), g=grid(1, 16, 16)) == E   # 1 video token > 0 rows
+    assert qknorm(lay=layout(batch=0), eps=0.0) == hv.HV_OK
+
+
+def test_qknorm_inconsistent_grid():
+    g = grid()
+    g.n_video = 39
+    assert qknorm(g=g) == E
