@@ -20,6 +20,13 @@ Each function restates, in NumPy float64, what the HunyuanVideo notes page
 * ``rms_norm_heads``  section 5.4, per-head RMSNorm of Q and K;
 * ``qk_norm_rope3d``  RMSNorm (video / text gamma, section 5.2) followed by the
                       3D RoPE of section 5.5;
+* ``attention_lse``   attention of query rows against a separate K/V block,
+                      with the log-sum-exp of each row (section 9.2, Ring
+                      Attention keeps query rows and passes K/V blocks);
+* ``merge_partials``  the exact combination of attention over disjoint key
+                      blocks from their outputs and log-sum-exps;
+* ``varlen_attention`` attention over packed segments (section 9.1, the
+                      variable-length FlashAttention call);
 * ``hot_path``        token grid, RoPE and attention in sequence.
 
 Nothing here is blocked, fused or reordered beyond the formulas: the matrix
@@ -31,7 +38,10 @@ angles, norm and relative-position invariants, the complex-number form of
 RoPE, uniform/one-key/two-key closed forms, permutation and shift
 invariance, masking with poisoned values, a pure-Python brute force, and for
 the RMSNorm unit output RMS, scale invariance, an epsilon closed form, head and
-channel isolation and the per-pair magnitudes that fix its order against RoPE.
+channel isolation and the per-pair magnitudes that fix its order against RoPE;
+for the log-sum-exp, merge and packed forms closed forms on one and repeated
+keys, the union identity, brute force, and agreement of the packed form with
+separate per-clip calls.
 """
 from .hv_oracle import (  # noqa: F401
     HEADS,
@@ -45,5 +55,8 @@ from .hv_oracle import (  # noqa: F401
     rms_norm_heads,
     qk_norm_rope3d,
     joint_attention,
+    attention_lse,
+    merge_partials,
+    varlen_attention,
     hot_path,
 )

@@ -193,6 +193,89 @@ def joint_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_video: int,
     return out
 
 
+def attention_lse(q: np.ndarray, k: np.ndarray, v: np.ndarray, k_len: Sequence[int],
+                  scale: Optional[float] = None,
+                  heads: Optional[Sequence[int]] = None):
+    """Exact softmax attention of every query row against the first k_len[b]
+    keys of batch entry b, with the log-sum-exp of its logits, float64.
+
+    ``q``: [B, Rq, H, D]; ``k``, ``v``: [B, Lk, H, D] (Rq and Lk independent,
+    as when a rank of a sequence-parallel ring holds its own query rows and
+    receives another rank's K/V block: notes page section 9.2).  Returns
+    (out [B, Rq, H', D], lse [B, H', Rq]) with
+        lse_i = log sum_j exp(scale * q_i . k_j),   out_i = sum_j exp(s_ij - lse_i) v_j.
+    """
+    B, Lk, H, D = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    heads = list(range(H)) if heads is None else list(heads)
+    Rq = q.shape[1]
+    out = np.zeros((B, Rq, len(heads), D), dtype=np.float64)
+    lse = np.zeros((B, len(heads), Rq), dtype=np.float64)
+    for b in range(B):
+        n = int(k_len[b])
+        if n <= 0 or n > Lk:
+            raise ValueError("k_len out of range")
+        for hi, h in enumerate(heads):
+            kb = np.ascontiguousarray(k[b, :n, h, :])
+            vb = np.ascontiguousarray(v[b, :n, h, :])
+            for s0 in range(0, Rq, 256):
+                scores = (q[b, s0:s0 + 256, h, :] @ kb.T) * scale
+                m = scores.max(axis=1, keepdims=True)
+                p = np.exp(scores - m)
+                z = p.sum(axis=1, keepdims=True)
+                out[b, s0:s0 + 256, hi, :] = (p @ vb) / z
+                lse[b, hi, s0:s0 + 256] = (m + np.log(z))[:, 0]
+    return out, lse
+
+
+def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[np.ndarray]):
+    """Combine attention results over disjoint key sets into the result over
+    their union, float64 (the Ring Attention half of USP, notes page section
+    9.2: each rank keeps its query rows and sees the K/V blocks one at a time).
+
+    For parts i with outputs O_i [B, R, H, D] and log-sum-exps lse_i [B, H, R]:
+        lse = log sum_i exp(lse_i),   O = sum_i exp(lse_i - lse) O_i.
+    This is the softmax over the union written per part, since part i's
+    unnormalised numerator is exp(lse_i) O_i.  Returns (O, lse).
+    """
+    lses = np.stack([np.asarray(x, dtype=np.float64) for x in lses])        # [P, B, H, R]
+    outs = np.stack([np.asarray(x, dtype=np.float64) for x in outs])        # [P, B, R, H, D]
+    top = lses.max(axis=0)
+    w = np.exp(lses - top)                                                  # [P, B, H, R]
+    total = w.sum(axis=0)
+    lse = top + np.log(total)
+    wt = np.transpose(w / total, (0, 1, 3, 2))[..., None]                   # [P, B, R, H, 1]
+    return (wt * outs).sum(axis=0), lse
+
+
+def varlen_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                     cu_q: Sequence[int], cu_k: Sequence[int],
+                     scale: Optional[float] = None,
+                     heads: Optional[Sequence[int]] = None):
+    """Exact attention over packed segments, float64 (the variable-length form
+    of FlashAttention that the model calls, notes page section 9.1).
+
+    ``q``, ``k``, ``v``: [T, H, D] packed rows.  Segment s owns query rows
+    [cu_q[s], cu_q[s+1]) and key rows [cu_k[s], cu_k[s+1]); its queries attend
+    to its keys only.  Returns (out [T, H', D], lse [H', T]); rows outside
+    every segment are left zero in both.
+    """
+    T, H, D = q.shape
+    heads = list(range(H)) if heads is None else list(heads)
+    out = np.zeros((T, len(heads), D), dtype=np.float64)
+    lse = np.zeros((len(heads), T), dtype=np.float64)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
+        if q1 == q0:
+            continue
+        o, l = attention_lse(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], [k1 - k0],
+                             scale=scale, heads=heads)
+        out[q0:q1] = o[0]
+        lse[:, q0:q1] = l[0]
+    return out, lse
+
+
 def hot_path(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
              frames: int, height: int, width: int, valid: Sequence[int],
              theta: float, rows: Optional[np.ndarray] = None,
