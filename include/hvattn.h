@@ -13,7 +13,10 @@
  *                 (separate video / text weights in double-stream blocks);
  *   - attention:  section 5.2 (joint softmax attention over [video; text],
  *                 scale 1/sqrt(128)); section 3.1 (at most 256 text tokens);
- *                 section 5.1 (24 heads x 128).
+ *                 section 5.1 (24 heads x 128);
+ *   - ring / varlen: section 9.2 (USP: Ring Attention passes K/V blocks, so
+ *                 partial results are merged by log-sum-exp); section 9.1
+ *                 (the variable-length FlashAttention call: packed segments).
  *
  * Conventions shared by all calls
  *   - Tensors are bfloat16 bit patterns (hv_bf16) in device memory owned by
@@ -51,6 +54,8 @@ extern "C" {
 #define HV_HEAD_DIM 128
 #define HV_MAX_BATCH 64
 #define HV_MAX_SEQ (1 << 24)
+#define HV_MAX_SEGMENTS 64    /* packed segments per varlen call */
+#define HV_MAX_MERGE_PARTS 16 /* partial results per merge call */
 
 typedef uint16_t hv_bf16; /* raw bfloat16 bits */
 
@@ -150,6 +155,71 @@ int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                            const int32_t* text_valid_len, hv_bf16* out,
                            const hv_layout* layout, int64_t n_video,
                            float softmax_scale, void* stream);
+
+/* hv_attention_fwd_lse: attention of query rows against a separate K/V
+ * block, with the log-sum-exp of every row, for sequence-parallel (ring)
+ * attention: notes page section 9.2 (USP; Ring Attention keeps each rank's
+ * query rows and passes K/V blocks around the ring).  Per batch entry b and
+ * head h, query row i attends to the first kv_valid_len[b] rows of k, v:
+ *   lse[b][h][i] = log sum_j exp(scale * q_i . k_j)       (natural log)
+ *   out_i        = sum_j exp(scale * q_i . k_j - lse) v_j
+ * Results over disjoint K/V blocks combine exactly with hv_attention_merge.
+ * bf16 inputs, fp32 accumulation, out rounded to bf16, lse fp32.
+ *   q, out        device pointers, layout *q_layout (out must not overlap
+ *                 q, k, v)
+ *   k, v          device pointers, layout *kv_layout; batch must equal
+ *                 q_layout->batch, seq_len (keys) may differ from q's
+ *   kv_valid_len  HOST array [batch] in [1, kv seq_len]; NULL = all keys
+ *   lse           device fp32 [batch][24][q seq_len], 4-byte aligned,
+ *                 disjoint from the tensors; NULL to skip
+ *   softmax_scale as in hv_joint_attention_fwd
+ * Errors: HV_ERR_INVALID_ARG (NULL, batch mismatch, valid length out of
+ * range, alignment, overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+int hv_attention_fwd_lse(const hv_bf16* q, const hv_layout* q_layout,
+                         const hv_bf16* k, const hv_bf16* v, const hv_layout* kv_layout,
+                         const int32_t* kv_valid_len, hv_bf16* out, float* lse,
+                         float softmax_scale, void* stream);
+
+/* hv_attention_merge: combine n_parts attention results computed over
+ * disjoint key blocks (e.g. by hv_attention_fwd_lse on each block of a ring)
+ * into the result over their union (notes page section 9.2):
+ *   lse = log sum_i exp(lse_i),   out = sum_i exp(lse_i - lse) outs[i]
+ * per (batch, row, head).  fp32 arithmetic, out rounded to bf16 once.
+ *   outs     HOST array of n_parts device pointers, each with *layout
+ *   lses     HOST array of n_parts device pointers, fp32 [batch][24][seq_len]
+ *   n_parts  1 .. HV_MAX_MERGE_PARTS
+ *   out      device pointer, *layout; must not overlap any input
+ *   lse_out  device fp32 [batch][24][seq_len] or NULL; must not overlap any
+ *            input or out
+ * A row whose lse_i are all -inf has no defined result (NaN).
+ * Errors: HV_ERR_INVALID_ARG (NULL, n_parts out of range, alignment,
+ * overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+int hv_attention_merge(const hv_bf16* const* outs, const float* const* lses,
+                       int32_t n_parts, hv_bf16* out, float* lse_out,
+                       const hv_layout* layout, void* stream);
+
+/* hv_joint_attention_varlen_fwd: attention over packed segments, the
+ * variable-length form of FlashAttention that the model calls (notes page
+ * section 9.1).  q, k, v, out hold T = layout->seq_len packed rows
+ * (layout->batch must be 1).  Segment s owns query rows
+ * [cu_seqlens_q[s], cu_seqlens_q[s+1]) and key rows
+ * [cu_seqlens_k[s], cu_seqlens_k[s+1]); its queries attend to its keys only.
+ * Several clips, each [video | valid text], pack back to back; the padded
+ * layout of hv_joint_attention_fwd is also expressible with each padded
+ * text tail as a segment of its own.  Output rows outside every segment
+ * are not written.
+ *   cu_seqlens_q/k  HOST arrays [n_segments + 1], non-decreasing, >= 0,
+ *                   last entry <= T; a segment with query rows needs >= 1 key
+ *   n_segments      1 .. HV_MAX_SEGMENTS
+ *   lse             device fp32 [24][T] (natural-log log-sum-exp per row) or
+ *                   NULL; rows outside every segment are not written
+ * Errors: HV_ERR_INVALID_ARG (NULL, batch != 1, bad offsets, alignment,
+ * overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t n_segments, hv_bf16* out, float* lse,
+                                  const hv_layout* layout, float softmax_scale,
+                                  void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* hv_status_string(int status);

@@ -12,6 +12,10 @@ not built, every call raises (there is no fallback).
                             gamma_q_text=None, gamma_k_text=None, eps=1e-6)
     hv_joint_attention_fwd(q, k, v, text_valid_len, n_video, out=None,
                            softmax_scale=None) -> out
+    hv_attention_fwd_lse(q, k, v, kv_valid_len=None, ...) -> (out, lse)
+    hv_attention_merge(outs, lses, ...) -> (out, lse)
+    hv_joint_attention_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None,
+                                  ...) -> (out, lse)
 """
 from __future__ import annotations
 
@@ -22,12 +26,15 @@ from typing import Optional, Sequence
 __all__ = [
     "HV_HEADS", "HV_HEAD_DIM", "HV_MAX_BATCH", "HvError", "HvGrid",
     "hv_token_grid", "hv_rope3d_apply", "hv_qk_norm_rope3d_apply", "hv_joint_attention_fwd",
+    "hv_attention_fwd_lse", "hv_attention_merge", "hv_joint_attention_varlen_fwd",
     "hv_status_string", "library_path", "load_library",
 ]
 
 HV_HEADS = 24
 HV_HEAD_DIM = 128
 HV_MAX_BATCH = 64
+HV_MAX_SEGMENTS = 64
+HV_MAX_MERGE_PARTS = 16
 HV_OK, HV_ERR_INVALID_ARG, HV_ERR_UNSUPPORTED, HV_ERR_HIP = 0, -1, -2, -3
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +110,22 @@ def load_library():
                                            ctypes.POINTER(_Layout), ctypes.c_int64, ctypes.c_float,
                                            ctypes.c_void_p]
     lib.hv_joint_attention_fwd.restype = ctypes.c_int
+    lib.hv_attention_fwd_lse.argtypes = [ctypes.c_void_p, ctypes.POINTER(_Layout), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.POINTER(_Layout),
+                                         ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
+    lib.hv_attention_fwd_lse.restype = ctypes.c_int
+    lib.hv_attention_merge.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.POINTER(_Layout), ctypes.c_void_p]
+    lib.hv_attention_merge.restype = ctypes.c_int
+    lib.hv_joint_attention_varlen_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.POINTER(ctypes.c_int32),
+                                                  ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                                  ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.POINTER(_Layout), ctypes.c_float,
+                                                  ctypes.c_void_p]
+    lib.hv_joint_attention_varlen_fwd.restype = ctypes.c_int
     lib.hv_status_string.argtypes = [ctypes.c_int]
     lib.hv_status_string.restype = ctypes.c_char_p
     lib.hv_version.argtypes = []
@@ -220,3 +243,121 @@ def hv_joint_attention_fwd(q, k, v, text_valid_len: Optional[Sequence[int]], n_v
     if st != HV_OK:
         raise HvError(st, "hv_joint_attention_fwd")
     return out
+
+
+def _lse_buffer(lse, shape, device, what: str):
+    import torch
+
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if lse.dtype != torch.float32 or lse.device != device or tuple(lse.shape) != tuple(shape) \
+            or not lse.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous float32 tensor of shape {tuple(shape)}")
+    return lse
+
+
+def hv_attention_fwd_lse(q, k, v, kv_valid_len: Optional[Sequence[int]] = None, out=None,
+                         lse=None, want_lse: bool = True, softmax_scale: Optional[float] = None):
+    """Attention of q's rows against a separate K/V block, with the natural-log
+    log-sum-exp of every row (see hvattn.h).  q: [B, Lq, 24, 128], k and v:
+    [B, Lk, 24, 128] (sharing shape and strides).  Returns (out, lse) with lse
+    float32 [B, 24, Lq] (None when want_lse is False and no lse is given)."""
+    import torch
+
+    qlay = _layout_of(q, "q")
+    kvlay = _layout_of(k, "k")
+    if not _same_layout(kvlay, _layout_of(v, "v")):
+        raise ValueError("k and v must share shape and strides")
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    elif not _same_layout(qlay, _layout_of(out, "out")):
+        raise ValueError("out must share shape and strides with q")
+    if lse is not None or want_lse:
+        lse = _lse_buffer(lse, (q.shape[0], HV_HEADS, q.shape[1]), q.device, "lse")
+    valid_arr = None
+    if kv_valid_len is not None:
+        vals = [int(x) for x in kv_valid_len]
+        if len(vals) != q.shape[0]:
+            raise ValueError("kv_valid_len needs one entry per batch element")
+        valid_arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = load_library().hv_attention_fwd_lse(q.data_ptr(), ctypes.byref(qlay), k.data_ptr(),
+                                             v.data_ptr(), ctypes.byref(kvlay), valid_arr,
+                                             out.data_ptr(), None if lse is None else lse.data_ptr(),
+                                             scale, _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_attention_fwd_lse")
+    return out, lse
+
+
+def hv_attention_merge(outs, lses, out=None, lse_out=None, want_lse: bool = True):
+    """Combine attention results over disjoint key blocks (see hvattn.h).
+    outs: list of [B, L, 24, 128] bf16 tensors sharing shape and strides; lses:
+    matching float32 [B, 24, L].  Returns (out, lse_out)."""
+    import torch
+
+    if len(outs) != len(lses) or not 1 <= len(outs) <= HV_MAX_MERGE_PARTS:
+        raise ValueError(f"need 1..{HV_MAX_MERGE_PARTS} (out, lse) pairs")
+    lay = _layout_of(outs[0], "outs[0]")
+    shape = (outs[0].shape[0], HV_HEADS, outs[0].shape[1])
+    for i, (o, l) in enumerate(zip(outs, lses)):
+        if not _same_layout(lay, _layout_of(o, f"outs[{i}]")):
+            raise ValueError("all partial outputs must share shape and strides")
+        _lse_buffer(l, shape, outs[0].device, f"lses[{i}]")
+    if out is None:
+        out = torch.empty_strided(outs[0].shape, outs[0].stride(), dtype=outs[0].dtype,
+                                  device=outs[0].device)
+    elif not _same_layout(lay, _layout_of(out, "out")):
+        raise ValueError("out must share shape and strides with the partial outputs")
+    if lse_out is not None or want_lse:
+        lse_out = _lse_buffer(lse_out, shape, outs[0].device, "lse_out")
+    n = len(outs)
+    optrs = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    lptrs = (ctypes.c_void_p * n)(*[l.data_ptr() for l in lses])
+    st = load_library().hv_attention_merge(optrs, lptrs, n, out.data_ptr(),
+                                           None if lse_out is None else lse_out.data_ptr(),
+                                           ctypes.byref(lay), _stream_of(out))
+    if st != HV_OK:
+        raise HvError(st, "hv_attention_merge")
+    return out, lse_out
+
+
+def hv_joint_attention_varlen_fwd(q, k, v, cu_seqlens_q: Sequence[int],
+                                  cu_seqlens_k: Optional[Sequence[int]] = None, out=None, lse=None,
+                                  want_lse: bool = False, softmax_scale: Optional[float] = None):
+    """Attention over packed segments (see hvattn.h).  q, k, v: [T, 24, 128]
+    packed rows sharing shape and strides; cu_seqlens_*: segment offsets
+    (cu_seqlens_k defaults to cu_seqlens_q).  Returns (out, lse) with lse
+    float32 [24, T] or None."""
+    import torch
+
+    def as4(t, name):
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [T, {HV_HEADS}, {HV_HEAD_DIM}]")
+        return t.unsqueeze(0)
+
+    q4, k4, v4 = as4(q, "q"), as4(k, "k"), as4(v, "v")
+    lay = _layout_of(q4, "q")
+    for t, name in ((k4, "k"), (v4, "v")):
+        if not _same_layout(lay, _layout_of(t, name)):
+            raise ValueError(f"q and {name} must share shape and strides")
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    elif not _same_layout(lay, _layout_of(as4(out, "out"), "out")):
+        raise ValueError("out must share shape and strides with q")
+    if lse is not None or want_lse:
+        lse = _lse_buffer(lse, (HV_HEADS, q.shape[0]), q.device, "lse")
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = cq if cu_seqlens_k is None else [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or len(cq) < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need n_segments + 1 entries each")
+    aq = (ctypes.c_int32 * len(cq))(*cq)
+    ak = (ctypes.c_int32 * len(ck))(*ck)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = load_library().hv_joint_attention_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), aq, ak,
+                                                      len(cq) - 1, out.data_ptr(),
+                                                      None if lse is None else lse.data_ptr(),
+                                                      ctypes.byref(lay), scale, _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_joint_attention_varlen_fwd")
+    return out, lse

@@ -190,31 +190,33 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const int hh = lane >> 5;
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous range of (batch, head, query-block) ids so that the query
+  // contiguous range of (segment, head, query-block) ids so that the query
   // blocks resident on one XCD stream the same K/V through its L2.
   const int nb = p.n_blocks;
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int per = nb >> 3, extra = nb & 7;
   const int logical = xcd * per + min(xcd, extra) + (bid >> 3);
-  const int qb = logical % p.n_qblocks;
-  const int bh = logical / p.n_qblocks;
-  const int head = bh % HV_HEADS;
-  const int b = bh / HV_HEADS;
+  int si = 0;  // segment of this block (uniform scan over at most 64 entries)
+  for (int i = 1; i < p.n_seg; ++i)
+    if (logical >= p.seg[i].blk_begin) si = i;
+  const AttnSegment& sg = p.seg[si];
+  const int rel = logical - sg.blk_begin;
+  const int head = rel / sg.nqb;
+  const int qb = rel - head * sg.nqb;
 
-  const int L = p.seq_len;
-  const int Lk = p.lk[b];
-  const int64_t sl = p.stride_l;
-  const int64_t hbase = (int64_t)b * p.stride_b + (int64_t)head * D;
-  const uint16_t* Kg = p.k + hbase;
-  const uint16_t* Vg = p.v + hbase;
+  const int L = sg.q_len;
+  const int Lk = sg.k_len;
+  const int64_t sl = p.kv_sl;
+  const uint16_t* Kg = p.k + sg.k_off + (int64_t)head * D;
+  const uint16_t* Vg = p.v + sg.k_off + (int64_t)head * D;
 
   // Q^T operand: lane holds query row q0 + l32, channels 16*kc + 8*hh .. +7.
   const int q0 = qb * BM + wave * QPW;
   const int qrow = min(q0 + l32, L - 1);  // rows past the end are computed, never stored
   bf16x8 qf[8];
   {
-    const uint16_t* qptr = p.q + hbase + (int64_t)qrow * sl + hh * 8;
+    const uint16_t* qptr = p.q + sg.q_off + (int64_t)head * D + (int64_t)qrow * p.q_sl + hh * 8;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) qf[kc] = *reinterpret_cast<const bf16x8*>(qptr + kc * 16);
   }
@@ -476,11 +478,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // no LDS access follows; drain the remaining (dead) tile loads before exit
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
-  // ---- epilogue: O / l, round to bf16, store rows that exist
-  const float inv = 1.0f / sum_across_halves(l_run);
+  // ---- epilogue: O / l, round to bf16, store rows that exist; optionally
+  // the natural-log log-sum-exp of the row's logits: the weights summed in l
+  // are 2^(s*c2 - m), so sum_j e^(scale*s_j) = 2^m * l.
+  const float l_tot = sum_across_halves(l_run);
+  const float inv = 1.0f / l_tot;
   const int orow = q0 + l32;
   if (orow < L) {
-    uint16_t* op = p.out + hbase + (int64_t)orow * sl;
+    uint16_t* op = p.out + sg.o_off + (int64_t)head * D + (int64_t)orow * p.o_sl;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -491,15 +496,25 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * j + 4 * hh) = w;
       }
     }
+    if (p.lse != nullptr && hh == 0)
+      p.lse[sg.lse_off + (int64_t)head * p.lse_hstride + orow] =
+          (m_run + __log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream) {
-  p.n_qblocks = (p.seq_len + BM - 1) / BM;
-  p.n_blocks = p.batch * HV_HEADS * p.n_qblocks;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)p.n_blocks), dim3(NT), 0, stream, p);
+  int blocks = 0;
+  for (int i = 0; i < p.n_seg; ++i) {
+    AttnSegment& sg = p.seg[i];
+    sg.nqb = (sg.q_len + BM - 1) / BM;
+    sg.blk_begin = blocks;
+    blocks += HV_HEADS * sg.nqb;
+  }
+  p.n_blocks = blocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -54,23 +54,63 @@ struct QkNormParams {
 
 hipError_t launch_qknorm_rope3d(const QkNormParams& p, hipStream_t stream);
 
-// ---- joint attention forward ----------------------------------------------
+// ---- attention forward ------------------------------------------------------
+// The kernel works on segments: segment s holds q_len query rows starting at
+// element q_off of q (token stride q_sl) and k_len keys starting at element
+// k_off of k and v (token stride kv_sl); its output rows start at element
+// o_off of out (stride o_sl).  A batch entry of the padded joint layout, a
+// packed clip and a (query rows, K/V block) pair of a ring step are all one
+// segment.  Query blocks of 256 rows are numbered segment by segment, head by
+// head: segment s owns logical blocks [blk_begin, blk_begin + 24 * nqb).
+constexpr int kMaxSegments = HV_MAX_SEGMENTS;
+
+struct AttnSegment {
+  int64_t q_off;     // elements
+  int64_t k_off;     // elements (k and v)
+  int64_t o_off;     // elements
+  int64_t lse_off;   // index of (head 0, row 0) in lse
+  int32_t q_len;     // query rows
+  int32_t k_len;     // keys, >= 1 when q_len > 0
+  int32_t blk_begin; // first logical block
+  int32_t nqb;       // query blocks per head
+};
+
 struct AttnParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* out;
+  float* lse;          // natural-log log-sum-exp per (head, row); may be null
+  int64_t q_sl;        // token strides, elements
+  int64_t kv_sl;
+  int64_t o_sl;
+  int64_t lse_hstride; // lse elements between heads
+  int32_t n_seg;
+  int32_t n_blocks;    // total logical blocks
+  float scale_log2;    // softmax scale * log2(e)
+  int32_t pad_;
+  AttnSegment seg[kMaxSegments];
+};
+
+// Fills blk_begin / nqb / n_blocks from q_len and launches.
+hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream);
+
+// ---- merge of partial attention results -------------------------------------
+// n_parts outputs over disjoint key blocks (same layout as out) and their
+// log-sum-exps ([batch][24][seq_len] fp32) combine into out / lse_out.
+struct MergeParams {
+  const uint16_t* outs[HV_MAX_MERGE_PARTS];
+  const float* lses[HV_MAX_MERGE_PARTS];
+  uint16_t* out;
+  float* lse_out;      // may be null
   int64_t stride_b;    // elements
   int64_t stride_l;    // elements
   int32_t batch;
   int32_t seq_len;
-  int32_t n_qblocks;   // query blocks per (batch, head)
-  int32_t n_blocks;    // batch * heads * n_qblocks
-  float scale_log2;    // softmax scale * log2(e)
+  int32_t n_parts;
   int32_t pad_;
-  int32_t lk[HV_MAX_BATCH];  // valid keys per batch entry (n_video + valid text)
 };
 
-hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace hv

@@ -53,6 +53,29 @@ bool overlap(const void* a, const void* b, const hv_layout* lay, int64_t elems) 
   return !(r >= kRowElems && sl - r >= kRowElems);
 }
 
+// Do the byte ranges [a, a + na) and [b, b + nb) meet?
+bool ranges_meet(const void* a, uintptr_t na, const void* b, uintptr_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na != 0 && nb != 0 && x < y + nb && y < x + na;
+}
+
+// Overlap of two bf16 tensors that may have different layouts: disjoint
+// ranges never overlap; same layouts use the exact row-interleave test;
+// anything else that shares bytes counts as overlapping.
+bool overlap_any(const void* a, int64_t ea, const void* b, int64_t eb, const hv_layout* la,
+                 const hv_layout* lb) {
+  if (!ranges_meet(a, (uintptr_t)ea * 2, b, (uintptr_t)eb * 2)) return false;
+  const bool same = la->batch == lb->batch && la->seq_len == lb->seq_len &&
+                    la->stride_b == lb->stride_b && la->stride_l == lb->stride_l;
+  return same ? overlap(a, b, la, ea) : true;
+}
+
+float scale_log2(float softmax_scale) {
+  float scale = softmax_scale;
+  if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf((float)HV_HEAD_DIM);
+  return (float)((double)scale * 1.4426950408889634);  // log2(e)
+}
+
 int check_grid(const hv_grid* g) {
   if (!g) return HV_ERR_INVALID_ARG;
   if (g->gt <= 0 || g->gh <= 0 || g->gw <= 0) return HV_ERR_INVALID_ARG;
@@ -212,20 +235,163 @@ int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
     const int64_t valid = text_valid_len ? text_valid_len[b] : text_cap;
     if (valid < 0 || valid > text_cap) return HV_ERR_INVALID_ARG;
     if (n_video + valid < 1) return HV_ERR_INVALID_ARG;
-    p.lk[b] = (int32_t)(n_video + valid);
+    hv::AttnSegment& sg = p.seg[b];
+    sg.q_off = sg.k_off = sg.o_off = (int64_t)b * layout->stride_b;
+    sg.q_len = layout->seq_len;
+    sg.k_len = (int32_t)(n_video + valid);
   }
-  float scale = softmax_scale;
-  if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf((float)HV_HEAD_DIM);
+  p.n_seg = layout->batch;
   p.q = q;
   p.k = k;
   p.v = v;
   p.out = out;
+  p.q_sl = p.kv_sl = p.o_sl = layout->stride_l;
+  p.scale_log2 = scale_log2(softmax_scale);
+  const hipError_t e = hv::launch_attn_fwd(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
+int hv_attention_fwd_lse(const hv_bf16* q, const hv_layout* q_layout, const hv_bf16* k,
+                         const hv_bf16* v, const hv_layout* kv_layout,
+                         const int32_t* kv_valid_len, hv_bf16* out, float* lse,
+                         float softmax_scale, void* stream) {
+  int64_t qext = 0, kvext = 0;
+  int st = check_layout(q_layout, &qext);
+  if (st != HV_OK) return st;
+  st = check_layout(kv_layout, &kvext);
+  if (st != HV_OK) return st;
+  if (kv_layout->batch != q_layout->batch) return HV_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out) return HV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HV_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u) != 0) return HV_ERR_INVALID_ARG;
+  const int B = q_layout->batch, Lq = q_layout->seq_len;
+  if (overlap(out, q, q_layout, qext) || overlap_any(out, qext, k, kvext, q_layout, kv_layout) ||
+      overlap_any(out, qext, v, kvext, q_layout, kv_layout))
+    return HV_ERR_INVALID_ARG;
+  if (lse) {
+    const int64_t n = (int64_t)B * HV_HEADS * Lq;
+    const uintptr_t lb = (uintptr_t)n * sizeof(float);
+    if (ranges_meet(lse, lb, q, qext * 2) || ranges_meet(lse, lb, out, qext * 2) ||
+        ranges_meet(lse, lb, k, kvext * 2) || ranges_meet(lse, lb, v, kvext * 2))
+      return HV_ERR_INVALID_ARG;
+  }
+  if (B == 0 || Lq == 0) return HV_OK;
+
+  hv::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = kv_valid_len ? kv_valid_len[b] : kv_layout->seq_len;
+    if (n < 1 || n > kv_layout->seq_len) return HV_ERR_INVALID_ARG;
+    hv::AttnSegment& sg = p.seg[b];
+    sg.q_off = sg.o_off = (int64_t)b * q_layout->stride_b;
+    sg.k_off = (int64_t)b * kv_layout->stride_b;
+    sg.lse_off = (int64_t)b * HV_HEADS * Lq;
+    sg.q_len = Lq;
+    sg.k_len = (int32_t)n;
+  }
+  p.n_seg = B;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.q_sl = p.o_sl = q_layout->stride_l;
+  p.kv_sl = kv_layout->stride_l;
+  p.lse_hstride = Lq;
+  p.scale_log2 = scale_log2(softmax_scale);
+  const hipError_t e = hv::launch_attn_fwd(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
+int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t n_segments, hv_bf16* out, float* lse,
+                                  const hv_layout* layout, float softmax_scale, void* stream) {
+  int64_t extent = 0;
+  int st = check_layout(layout, &extent);
+  if (st != HV_OK) return st;
+  if (layout->batch != 1) return HV_ERR_INVALID_ARG;
+  if (n_segments < 1 || n_segments > HV_MAX_SEGMENTS) return HV_ERR_INVALID_ARG;
+  if (!cu_seqlens_q || !cu_seqlens_k) return HV_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out) return HV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HV_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u) != 0) return HV_ERR_INVALID_ARG;
+  if (overlap(out, q, layout, extent) || overlap(out, k, layout, extent) ||
+      overlap(out, v, layout, extent))
+    return HV_ERR_INVALID_ARG;
+  const int T = layout->seq_len;
+  if (lse) {
+    const uintptr_t lb = (uintptr_t)HV_HEADS * T * sizeof(float);
+    if (ranges_meet(lse, lb, q, extent * 2) || ranges_meet(lse, lb, out, extent * 2) ||
+        ranges_meet(lse, lb, k, extent * 2) || ranges_meet(lse, lb, v, extent * 2))
+      return HV_ERR_INVALID_ARG;
+  }
+  hv::AttnParams p;
+  memset(&p, 0, sizeof(p));
+  if (cu_seqlens_q[0] < 0 || cu_seqlens_k[0] < 0) return HV_ERR_INVALID_ARG;
+  for (int s = 0; s < n_segments; ++s) {
+    const int32_t q0 = cu_seqlens_q[s], q1 = cu_seqlens_q[s + 1];
+    const int32_t k0 = cu_seqlens_k[s], k1 = cu_seqlens_k[s + 1];
+    if (q1 < q0 || k1 < k0 || q1 > T || k1 > T) return HV_ERR_INVALID_ARG;
+    if (q1 > q0 && k1 == k0) return HV_ERR_INVALID_ARG;  // queries with no key
+    hv::AttnSegment& sg = p.seg[s];
+    sg.q_off = sg.o_off = (int64_t)q0 * layout->stride_l;
+    sg.k_off = (int64_t)k0 * layout->stride_l;
+    sg.lse_off = q0;
+    sg.q_len = q1 - q0;
+    sg.k_len = k1 - k0;
+  }
+  if (T == 0) return HV_OK;
+  p.n_seg = n_segments;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.q_sl = p.kv_sl = p.o_sl = layout->stride_l;
+  p.lse_hstride = T;
+  p.scale_log2 = scale_log2(softmax_scale);
+  const hipError_t e = hv::launch_attn_fwd(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
+int hv_attention_merge(const hv_bf16* const* outs, const float* const* lses, int32_t n_parts,
+                       hv_bf16* out, float* lse_out, const hv_layout* layout, void* stream) {
+  int64_t extent = 0;
+  int st = check_layout(layout, &extent);
+  if (st != HV_OK) return st;
+  if (n_parts < 1 || n_parts > HV_MAX_MERGE_PARTS) return HV_ERR_INVALID_ARG;
+  if (!outs || !lses || !out) return HV_ERR_INVALID_ARG;
+  if (!aligned16(out)) return HV_ERR_INVALID_ARG;
+  if (lse_out && ((uintptr_t)lse_out & 3u) != 0) return HV_ERR_INVALID_ARG;
+  const int64_t nl = (int64_t)layout->batch * HV_HEADS * layout->seq_len;
+  const uintptr_t lb = (uintptr_t)nl * sizeof(float);
+  for (int i = 0; i < n_parts; ++i) {
+    if (!outs[i] || !lses[i]) return HV_ERR_INVALID_ARG;
+    if (!aligned16(outs[i]) || ((uintptr_t)lses[i] & 3u) != 0) return HV_ERR_INVALID_ARG;
+    if (overlap(out, outs[i], layout, extent)) return HV_ERR_INVALID_ARG;
+    if (ranges_meet(lses[i], lb, out, extent * 2)) return HV_ERR_INVALID_ARG;
+    if (lse_out && (ranges_meet(lse_out, lb, lses[i], lb) ||
+                    ranges_meet(lse_out, lb, outs[i], extent * 2)))
+      return HV_ERR_INVALID_ARG;
+  }
+  if (lse_out && ranges_meet(lse_out, lb, out, extent * 2)) return HV_ERR_INVALID_ARG;
+  if (layout->batch == 0 || layout->seq_len == 0) return HV_OK;
+
+  hv::MergeParams p;
+  memset(&p, 0, sizeof(p));
+  for (int i = 0; i < n_parts; ++i) {
+    p.outs[i] = outs[i];
+    p.lses[i] = lses[i];
+  }
+  p.n_parts = n_parts;
+  p.out = out;
+  p.lse_out = lse_out;
   p.stride_b = layout->stride_b;
   p.stride_l = layout->stride_l;
   p.batch = layout->batch;
   p.seq_len = layout->seq_len;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
-  const hipError_t e = hv::launch_attn_fwd(p, (hipStream_t)stream);
+  const hipError_t e = hv::launch_attn_merge(p, (hipStream_t)stream);
   return e == hipSuccess ? HV_OK : HV_ERR_HIP;
 }
 

@@ -244,3 +244,108 @@ def test_qknorm_inconsistent_grid():
     g = grid()
     g.n_video = 39
     assert qknorm(g=g) == E
+
+
+# --------------------------------------- attention with LSE, merge, varlen
+LSE = FAKE + 8 * SEP
+
+
+def attn_lse(q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP, out=FAKE + 3 * SEP, lse=LSE, valid=None,
+             qlay=None, kvlay=None, scale=0.0):
+    lib = hv.load_library()
+    qlay = layout(seq=200) if qlay is None else qlay
+    kvlay = layout(seq=300) if kvlay is None else kvlay
+    arr = None if valid is None else (ctypes.c_int32 * max(1, len(valid)))(*valid)
+    return lib.hv_attention_fwd_lse(q, ctypes.byref(qlay) if qlay is not False else None, k, v,
+                                    ctypes.byref(kvlay) if kvlay is not False else None, arr, out,
+                                    lse, scale, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(k=0), E), (dict(v=0), E), (dict(out=0), E),
+    (dict(qlay=False), E), (dict(kvlay=False), E),
+    (dict(qlay=layout(batch=2, seq=200)), E),                 # batch mismatch
+    (dict(valid=(0,)), E), (dict(valid=(301,)), E), (dict(valid=(-4,)), E),
+    (dict(lse=LSE + 2), E),                                   # lse alignment
+    (dict(out=FAKE + 2 * SEP + 4096), E),                     # out inside v (other layout)
+    (dict(out=FAKE + 100 * 3072 * 2), E),                     # out inside q
+    (dict(lse=FAKE + SEP + 64), E),                           # lse inside k
+    (dict(lse=FAKE + 3 * SEP + 8), E),                        # lse inside out
+    (dict(qlay=layout(seq=200, heads=8)), U), (dict(kvlay=layout(seq=300, dim=64)), U),
+    (dict(kvlay=layout(seq=300, sl=3076)), E),
+])
+def test_attention_lse_validation(kwargs, expect):
+    assert attn_lse(**kwargs) == expect
+
+
+def test_attention_lse_empty_and_optional_lse():
+    assert attn_lse(qlay=layout(batch=0, seq=200), kvlay=layout(batch=0, seq=300)) == hv.HV_OK
+    assert attn_lse(qlay=layout(seq=0, sb=0)) == hv.HV_OK
+    # lse = NULL passes validation as well (empty call: nothing launched)
+    assert attn_lse(lse=None, qlay=layout(seq=0, sb=0)) == hv.HV_OK
+
+
+def merge(outs=None, lses=None, n=None, out=FAKE + 3 * SEP, lse_out=FAKE + 9 * SEP, lay=None):
+    lib = hv.load_library()
+    outs = [FAKE, FAKE + SEP] if outs is None else outs
+    lses = [FAKE + 6 * SEP, FAKE + 7 * SEP] if lses is None else lses
+    n = len(outs) if n is None else n
+    oa = (ctypes.c_void_p * max(1, len(outs)))(*outs)
+    la = (ctypes.c_void_p * max(1, len(lses)))(*lses)
+    lay = layout() if lay is None else lay
+    return lib.hv_attention_merge(oa, la, n, out, lse_out, ctypes.byref(lay), None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(n=0), E), (dict(outs=[FAKE] * 17, lses=[FAKE + 6 * SEP] * 17), E),
+    (dict(outs=[FAKE, 0]), E), (dict(lses=[FAKE + 6 * SEP, 0]), E), (dict(out=0), E),
+    (dict(outs=[FAKE, FAKE + SEP + 8]), E), (dict(lses=[FAKE + 6 * SEP, FAKE + 7 * SEP + 2]), E),
+    (dict(out=FAKE + 3 * SEP + 4), E), (dict(lse_out=FAKE + 9 * SEP + 1), E),
+    (dict(out=FAKE + SEP), E),                                # out is a partial output
+    (dict(lse_out=FAKE + 7 * SEP), E),                        # lse_out is a partial lse
+    (dict(lse_out=FAKE + 3 * SEP + 64), E),                   # lse_out inside out
+    (dict(lses=[FAKE + 3 * SEP + 128, FAKE + 7 * SEP]), E),   # an input lse inside out
+    (dict(lay=layout(heads=12)), U),
+])
+def test_merge_validation(kwargs, expect):
+    assert merge(**kwargs) == expect
+
+
+def test_merge_accepts_16_parts_and_null_lse_out_when_empty():
+    outs = [FAKE + i * (1 << 30) for i in range(16)]
+    lses = [FAKE + 12 * SEP + i * (1 << 30) for i in range(16)]
+    assert merge(outs=outs, lses=lses, out=FAKE + 30 * SEP, lse_out=None,
+                 lay=layout(batch=0)) == hv.HV_OK
+
+
+def varlen(cq=(0, 100, 300), ck=None, n=None, q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP,
+           out=FAKE + 3 * SEP, lse=LSE, lay=None):
+    lib = hv.load_library()
+    ck = cq if ck is None else ck
+    n = len(cq) - 1 if n is None else n
+    aq = (ctypes.c_int32 * len(cq))(*cq)
+    ak = (ctypes.c_int32 * len(ck))(*ck)
+    lay = layout() if lay is None else lay
+    return lib.hv_joint_attention_varlen_fwd(q, k, v, aq, ak, n, out, lse, ctypes.byref(lay), 0.0, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(k=0), E), (dict(v=0), E), (dict(out=0), E),
+    (dict(n=0), E), (dict(n=65, cq=tuple(range(66)), ck=tuple(range(66))), E),
+    (dict(cq=(0, 100, 301)), E),                              # past the packed rows
+    (dict(cq=(0, 120, 100)), E),                              # decreasing
+    (dict(cq=(-1, 100, 300)), E),
+    (dict(cq=(0, 100, 300), ck=(0, 100, 100)), E),            # queries without keys
+    (dict(lay=layout(batch=2, sb=300 * 3072)), E),            # packed layout has batch 1
+    (dict(lse=LSE + 2), E), (dict(lse=FAKE + 40), E),         # lse inside q
+    (dict(out=FAKE + SEP + 3072 * 2 * 5), E),                 # out inside k
+    (dict(lay=layout(heads=12)), U),
+])
+def test_varlen_validation(kwargs, expect):
+    assert varlen(**kwargs) == expect
+
+
+def test_varlen_empty_segments_are_valid():
+    # all-empty segments: nothing to launch
+    assert varlen(cq=(0, 0, 0), ck=(0, 0, 5)) == hv.HV_OK
+    assert varlen(cq=(0, 0), ck=(0, 0), lay=layout(seq=0, sb=0)) == hv.HV_OK
