@@ -15,7 +15,10 @@ per-kernel times from HIP events on the launch stream, the attention
 kernel's MFMA roofline fraction, and the fp64 oracle timed on a bounded
 sample of the same workload on the host cores.  The QK-norm + RoPE prologue
 (hv_qk_norm_rope3d_apply, all rows of q and k) is timed separately on the
-same resident tensors and reported beside the step (qknorm_rope_*).
+same resident tensors and reported beside the step (qknorm_rope_*).  The
+`extras` object times one rank's share of an 8-way ring attention (partial
+attention per K/V block plus the log-sum-exp merge) and a packed
+variable-length call (--no-extras skips them).
 """
 from __future__ import annotations
 
@@ -99,6 +102,88 @@ def cpu_baseline(bits, wl, n_video, seq_len, rows_n: int):
     }
 
 
+def timed(torch, stream, fn, reps: int) -> float:
+    """Average ms of fn() over reps calls, HIP events on the launch stream."""
+    fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        fn()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int) -> dict:
+    """Measurements of the sequence-parallel and packed attention forms on the
+    resident tensors (not part of the timed step).
+
+    ring8_rank: one rank's share of an 8-way ring at this size: L/8 query
+      rows against the 8 K/V blocks of L/8 keys (8 hv_attention_fwd_lse calls)
+      plus the hv_attention_merge of the 8 partial results.
+    merge8: that merge alone, against HBM (reads 8 partial outputs and
+      log-sum-exps, writes one of each).
+    varlen_pack: the batch of two 720x1280x33 clips with 37 and 256 valid text
+      tokens packed as [valid | padded tail] segments of one sequence (the
+      padded tails attend to themselves), one hv_joint_attention_varlen_fwd.
+    """
+    out = {}
+    P = 8
+    Lr = L // P
+    bounds = [i * Lr for i in range(P)] + [L]
+    valid_total = grid.n_video + wl.valid[0]
+    qr = q[:1, :Lr]
+    parts = []
+    for a, b in zip(bounds, bounds[1:]):
+        n = min(b, valid_total) - a
+        if n > 0:
+            parts.append((a, b, n))
+    po = [torch.empty_like(qr) for _ in parts]
+    pl = [torch.empty((1, HEADS, Lr), dtype=torch.float32, device=q.device) for _ in parts]
+    mo = torch.empty_like(qr)
+    ml = torch.empty((1, HEADS, Lr), dtype=torch.float32, device=q.device)
+
+    def partials():
+        for (a, b, n), o, l in zip(parts, po, pl):
+            hv.hv_attention_fwd_lse(qr, k[:1, a:b], v[:1, a:b], [n], out=o, lse=l)
+
+    def merge():
+        hv.hv_attention_merge(po, pl, out=mo, lse_out=ml)
+
+    ms_part = timed(torch, stream, partials, reps)
+    ms_merge = timed(torch, stream, merge, reps)
+    fl = 4.0 * HEADS * HEAD_DIM * Lr * sum(n for _, _, n in parts)
+    mbytes = (len(parts) + 1) * (Lr * HEADS * HEAD_DIM * 2 + Lr * HEADS * 4)
+    out["ring8_rank"] = {"q_rows": Lr, "kv_blocks": len(parts), "ms": round(ms_part + ms_merge, 4),
+                         "attn_ms": round(ms_part, 4),
+                         "tflops": round(fl / ((ms_part + ms_merge) / 1e3) / 1e12, 2),
+                         "attn_tflops": round(fl / (ms_part / 1e3) / 1e12, 2)}
+    out["merge8"] = {"ms": round(ms_merge, 4), "bytes": mbytes,
+                     "GBps": round(mbytes / (ms_merge / 1e3) / 1e9, 1),
+                     "pct_hbm_peak": round(100.0 * mbytes / (ms_merge / 1e3) / 1e9 / PEAK_HBM_GBPS, 2)}
+    del po, pl, mo, ml
+
+    wb = hvinputs.WORKLOADS["video_720x1280x33_b2"]
+    gb = hv.hv_token_grid(wb.frames, wb.height, wb.width)
+    Lb = gb.n_video + wb.text_capacity
+    T = wb.batch * Lb
+    if T <= q.shape[1]:
+        qp, kp, vp = (t[0, :T] for t in (q, k, v))
+        cu = [0]
+        seg_pairs = []
+        for b in range(wb.batch):
+            n = gb.n_video + wb.valid[b]
+            cu += [b * Lb + n, (b + 1) * Lb]
+            seg_pairs += [n * n, (Lb - n) ** 2]
+        op = torch.empty_like(qp)
+        ms_v = timed(torch, stream, lambda: hv.hv_joint_attention_varlen_fwd(qp, kp, vp, cu, out=op), reps)
+        flv = 4.0 * HEADS * HEAD_DIM * sum(seg_pairs)
+        out["varlen_pack"] = {"workload": wb.name, "segments": len(cu) - 1, "rows": T,
+                              "ms": round(ms_v, 4), "tflops": round(flv / (ms_v / 1e3) / 1e12, 2)}
+        del op
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +191,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the ring-attention and packed-segment measurements")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -254,6 +341,9 @@ def main() -> int:
             "traffic": traffic,
         },
     }
+    if not args.no_extras:
+        result["extras"] = extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream,
+                                      max(3, args.steps // 4))
     del q, k, v, out
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
