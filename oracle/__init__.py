@@ -27,6 +27,9 @@ Each function restates, in NumPy float64, what the HunyuanVideo notes page
                       blocks from their outputs and log-sum-exps;
 * ``varlen_attention`` attention over packed segments (section 9.1, the
                       variable-length FlashAttention call);
+* ``joint_attention_bwd`` gradients dQ, dK, dV of the joint attention (the
+                      report summary page's training-side attention cost),
+                      by the chain rule through the softmax;
 * ``hot_path``        token grid, RoPE and attention in sequence.
 
 Nothing here is blocked, fused or reordered beyond the formulas: the matrix
@@ -41,7 +44,8 @@ the RMSNorm unit output RMS, scale invariance, an epsilon closed form, head and
 channel isolation and the per-pair magnitudes that fix its order against RoPE;
 for the log-sum-exp, merge and packed forms closed forms on one and repeated
 keys, the union identity, brute force, and agreement of the packed form with
-separate per-clip calls.
+separate per-clip calls; for the gradients central finite differences of the
+oracle's own forward, and the shift and sum identities they obey.
 """
 from .hv_oracle import (  # noqa: F401
     HEADS,
@@ -58,5 +62,6 @@ from .hv_oracle import (  # noqa: F401
     attention_lse,
     merge_partials,
     varlen_attention,
+    joint_attention_bwd,
     hot_path,
 )

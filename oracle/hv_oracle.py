@@ -276,6 +276,48 @@ def varlen_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return out, lse
 
 
+def joint_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                        n_video: int, valid: Sequence[int], scale: Optional[float] = None,
+                        heads: Optional[Sequence[int]] = None):
+    """Gradients of the joint attention of ``joint_attention``, float64.
+
+    With O = softmax(scale * Q K^T) V over the valid keys of each batch entry
+    (the attention the report summary page names as the training bottleneck,
+    "FusedAttention" in its Infra section) and an upstream gradient dO, the
+    chain rule through the softmax gives, per (batch, head):
+        P  = softmax(scale * Q K^T),       dV = P^T dO,
+        dP = dO V^T,                        dS = P * (dP - rowsum(P * dP)),
+        dQ = scale * dS K,                  dK = scale * dS^T Q.
+    Padded keys take no part, so their dK, dV are zero.  All query rows
+    (padded text rows included) contribute, as in the forward.
+    ``q``, ``k``, ``v``, ``dout``: [B, L, H, D].  Returns (dq, dk, dv), each
+    [B, L, H', D] for the heads listed in ``heads``.
+    """
+    B, L, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    heads = list(range(H)) if heads is None else list(heads)
+    dq = np.zeros((B, L, len(heads), D), dtype=np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    for b in range(B):
+        lk = n_video + int(valid[b])
+        if lk <= 0:
+            raise ValueError("no valid keys")
+        for hi, h in enumerate(heads):
+            qb, kb, vb, gb = (np.ascontiguousarray(t[b, :, h, :]) for t in (q, k, v, dout))
+            kb, vb = kb[:lk], vb[:lk]
+            s = (qb @ kb.T) * scale
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = gb @ vb.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, :, hi, :] = scale * (ds @ kb)
+            dk[b, :lk, hi, :] = scale * (ds.T @ qb)
+            dv[b, :lk, hi, :] = p.T @ gb
+    return dq, dk, dv
+
+
 def hot_path(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
              frames: int, height: int, width: int, valid: Sequence[int],
              theta: float, rows: Optional[np.ndarray] = None,
