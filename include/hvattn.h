@@ -14,6 +14,8 @@
  *   - attention:  section 5.2 (joint softmax attention over [video; text],
  *                 scale 1/sqrt(128)); section 3.1 (at most 256 text tokens);
  *                 section 5.1 (24 heads x 128);
+ *   - backward:   the report summary page's Infra section (training:
+ *                 fused attention is the bottleneck);
  *   - ring / varlen: section 9.2 (USP: Ring Attention passes K/V blocks, so
  *                 partial results are merged by log-sum-exp); section 9.1
  *                 (the variable-length FlashAttention call: packed segments).
@@ -220,6 +222,34 @@ int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_b
                                   int32_t n_segments, hv_bf16* out, float* lse,
                                   const hv_layout* layout, float softmax_scale,
                                   void* stream);
+
+/* hv_joint_attention_bwd: gradients of hv_joint_attention_fwd by the chain
+ * rule through the softmax (the training-side attention cost the report
+ * summary page names, "FusedAttention" in its Infra section).  Per (batch,
+ * head), with P = softmax(scale * Q K^T) over the valid keys:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ * Padded keys (>= n_video + text_valid_len[b]) get dk = dv = 0; every query
+ * row contributes.  P is recomputed from lse.  bf16 in and out, fp32
+ * accumulation; P and dS are rounded to bf16 as MFMA operands.
+ *   q, k, v, out, dout  device pointers, layout *layout; out is the forward's
+ *                       output and dout the gradient with respect to it
+ *   lse                 device fp32 [batch][24][seq_len]: the natural-log
+ *                       log-sum-exp of the forward, as hv_attention_fwd_lse
+ *                       writes it for the same q, k, v and valid keys
+ *   text_valid_len, n_video, softmax_scale  as in hv_joint_attention_fwd
+ *   dq, dk, dv          device pointers, layout *layout; must not overlap any
+ *                       input or each other
+ *   delta               device fp32 [batch][24][seq_len] workspace, written
+ *                       with rowsum(dO * O) (caller-owned, disjoint from all
+ *                       other arguments)
+ * Errors: HV_ERR_INVALID_ARG (NULL, valid length out of range, alignment,
+ * overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                           const hv_bf16* out, const hv_bf16* dout, const float* lse,
+                           const int32_t* text_valid_len, int64_t n_video,
+                           hv_bf16* dq, hv_bf16* dk, hv_bf16* dv, float* delta,
+                           const hv_layout* layout, float softmax_scale, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* hv_status_string(int status);

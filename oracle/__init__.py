@@ -29,7 +29,8 @@ Each function restates, in NumPy float64, what the HunyuanVideo notes page
                       variable-length FlashAttention call);
 * ``joint_attention_bwd`` gradients dQ, dK, dV of the joint attention (the
                       report summary page's training-side attention cost),
-                      by the chain rule through the softmax;
+                      by the chain rule through the softmax
+                      (``joint_attention_bwd_dq_rows``: dQ of selected rows);
 * ``hot_path``        token grid, RoPE and attention in sequence.
 
 Nothing here is blocked, fused or reordered beyond the formulas: the matrix
@@ -63,5 +64,6 @@ from .hv_oracle import (  # noqa: F401
     merge_partials,
     varlen_attention,
     joint_attention_bwd,
+    joint_attention_bwd_dq_rows,
     hot_path,
 )

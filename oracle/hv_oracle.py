@@ -318,6 +318,40 @@ def joint_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.nd
     return dq, dk, dv
 
 
+def joint_attention_bwd_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                                n_video: int, valid: Sequence[int],
+                                scale: Optional[float] = None,
+                                heads: Optional[Sequence[int]] = None) -> np.ndarray:
+    """dQ of ``joint_attention_bwd`` for a subset of query rows.
+
+    A query row's gradient needs only its own softmax row: P_i over the valid
+    keys, dP_i = dO_i V^T and dS_i = P_i * (dP_i - sum_j P_ij dP_ij), then
+    dQ_i = scale * dS_i K.  ``q`` and ``dout`` hold the selected rows
+    ([B, R, H, D]); ``k``, ``v`` all rows.  Returns [B, R, H', D].
+    """
+    B, L, H, D = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    heads = list(range(H)) if heads is None else list(heads)
+    R = q.shape[1]
+    dq = np.zeros((B, R, len(heads), D), dtype=np.float64)
+    for b in range(B):
+        lk = n_video + int(valid[b])
+        for hi, h in enumerate(heads):
+            kb = np.ascontiguousarray(k[b, :lk, h, :])
+            vb = np.ascontiguousarray(v[b, :lk, h, :])
+            for s0 in range(0, R, 256):
+                qb = q[b, s0:s0 + 256, h, :]
+                gb = dout[b, s0:s0 + 256, h, :]
+                sc = (qb @ kb.T) * scale
+                p = np.exp(sc - sc.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                dp = gb @ vb.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, s0:s0 + 256, hi, :] = scale * (ds @ kb)
+    return dq
+
+
 def hot_path(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
              frames: int, height: int, width: int, valid: Sequence[int],
              theta: float, rows: Optional[np.ndarray] = None,

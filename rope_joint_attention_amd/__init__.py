@@ -16,6 +16,8 @@ not built, every call raises (there is no fallback).
     hv_attention_merge(outs, lses, ...) -> (out, lse)
     hv_joint_attention_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None,
                                   ...) -> (out, lse)
+    hv_joint_attention_bwd(q, k, v, out, dout, lse, text_valid_len, n_video,
+                           ...) -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ __all__ = [
     "HV_HEADS", "HV_HEAD_DIM", "HV_MAX_BATCH", "HvError", "HvGrid",
     "hv_token_grid", "hv_rope3d_apply", "hv_qk_norm_rope3d_apply", "hv_joint_attention_fwd",
     "hv_attention_fwd_lse", "hv_attention_merge", "hv_joint_attention_varlen_fwd",
+    "hv_joint_attention_bwd",
     "hv_status_string", "library_path", "load_library",
 ]
 
@@ -126,6 +129,10 @@ def load_library():
                                                   ctypes.POINTER(_Layout), ctypes.c_float,
                                                   ctypes.c_void_p]
     lib.hv_joint_attention_varlen_fwd.restype = ctypes.c_int
+    lib.hv_joint_attention_bwd.argtypes = [ctypes.c_void_p] * 6 + [
+        ctypes.POINTER(ctypes.c_int32), ctypes.c_int64] + [ctypes.c_void_p] * 4 + [
+        ctypes.POINTER(_Layout), ctypes.c_float, ctypes.c_void_p]
+    lib.hv_joint_attention_bwd.restype = ctypes.c_int
     lib.hv_status_string.argtypes = [ctypes.c_int]
     lib.hv_status_string.restype = ctypes.c_char_p
     lib.hv_version.argtypes = []
@@ -361,3 +368,43 @@ def hv_joint_attention_varlen_fwd(q, k, v, cu_seqlens_q: Sequence[int],
     if st != HV_OK:
         raise HvError(st, "hv_joint_attention_varlen_fwd")
     return out, lse
+
+
+def hv_joint_attention_bwd(q, k, v, out, dout, lse, text_valid_len: Optional[Sequence[int]],
+                           n_video: int, dq=None, dk=None, dv=None, delta=None,
+                           softmax_scale: Optional[float] = None):
+    """Gradients of hv_joint_attention_fwd (see hvattn.h).  q, k, v, out, dout
+    share shape [B, L, 24, 128] and strides; lse is the forward's float32
+    [B, 24, L] log-sum-exp (hv_attention_fwd_lse).  Returns (dq, dk, dv)."""
+    import torch
+
+    lay = _layout_of(q, "q")
+    for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        if not _same_layout(lay, _layout_of(t, name)):
+            raise ValueError(f"q and {name} must share shape and strides")
+    shape = (q.shape[0], HV_HEADS, q.shape[1])
+    _lse_buffer(lse, shape, q.device, "lse")
+    delta = _lse_buffer(delta, shape, q.device, "delta")
+    grads = []
+    for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if g is None:
+            g = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        elif not _same_layout(lay, _layout_of(g, name)):
+            raise ValueError(f"{name} must share shape and strides with q")
+        grads.append(g)
+    valid_arr = None
+    if text_valid_len is not None:
+        vals = [int(x) for x in text_valid_len]
+        if len(vals) != q.shape[0]:
+            raise ValueError("text_valid_len needs one entry per batch element")
+        valid_arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = load_library().hv_joint_attention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                               valid_arr, int(n_video), grads[0].data_ptr(),
+                                               grads[1].data_ptr(), grads[2].data_ptr(),
+                                               delta.data_ptr(), ctypes.byref(lay), scale,
+                                               _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_joint_attention_bwd")
+    return tuple(grads)

@@ -1,0 +1,496 @@
+// Gradients of the joint [video; text] attention for gfx950 (MI355X).
+//
+// What is computed: the attention of the HunyuanVideo notes page ("HunyuanVideo
+// 模型结构与数学原理", section 5.2) differentiated by the chain rule through the
+// softmax; the report summary page (zhao9797.github.io, "hunyuan-video", Infra
+// section, training) names fused attention as the training bottleneck.  Per
+// (batch, head), with P = softmax(scale * Q K^T) over the valid keys and the
+// upstream gradient dO:
+//     D_i = sum_c dO_ic O_ic             (= rowsum(P * dP), since O = P V)
+//     dV  = P^T dO,   dP = dO V^T,   dS = P * (dP - D),
+//     dQ  = scale * dS K,   dK = scale * dS^T Q.
+// P is recomputed from the forward's log-sum-exp: P_ij = exp(scale s_ij - lse_i),
+// so no running maximum is needed.  Padded keys get zero dK, dV.
+//
+// Three kernels, all MFMA 32x32x16 bf16 with fp32 accumulation:
+//   * delta: D per (row, head), one thread per 16-byte chunk, 16-lane DPP sum;
+//   * dkdv:  one workgroup per (batch, head, 128 keys), 4 waves of 32 keys,
+//            K and V of its keys held in registers as MFMA operands; it walks
+//            all query tiles of 64 rows (Q, dO, lse, D staged in LDS by
+//            global->LDS loads, two stages) and accumulates dV^T += dO^T P and
+//            dK^T += Q^T dS in registers;
+//   * dq:    one workgroup per (batch, head, 128 queries), 4 waves of 32
+//            queries with Q and dO in registers; it walks the key tiles of 64
+//            rows (K, V staged the same way) and accumulates dQ^T += K^T dS^T.
+// dQ is computed in its own pass (recomputing S and dP) instead of by atomics
+// from the key-block kernel: no fp32 scratch, deterministic results.
+//
+// Orientation.  Scores are formed so that the lane owns the row whose
+// statistics it needs: in dq, S^T = K Q^T (lane = query, one lse and one D per
+// lane); in dkdv, S = Q K^T (lane = key), and the per-query lse and D of the
+// 16 rows a lane holds are read from LDS as four 16-byte vectors.  The
+// operand that has to be transposed (K^T in dq, dO^T and Q^T in dkdv) comes
+// from LDS through ds_read_b64_tr_b16, as V^T does in the forward kernel.
+//
+// LDS tiles are 64 rows of 256 bytes; the 16-byte chunk c of row r is stored
+// at slot c ^ f(r mod 16) with f(r) = 4(r mod 4) + (r div 4) mod 4.  Sixteen
+// consecutive rows at one chunk (the row-operand reads) hit 16 distinct slots,
+// and eight rows (a multiple of 8 onwards) by four chunks (the transposing
+// reads) hit 16 distinct slots twice each, so both read patterns are free of
+// bank conflicts on the same tile.
+#include <type_traits>
+
+#include "hv_internal.h"
+
+namespace hv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define HV_LDS __attribute__((address_space(3)))
+
+constexpr int D = HV_HEAD_DIM;   // 128
+constexpr int ROWB = D * 2;      // bytes per tile row
+constexpr int TR = 64;           // rows per staged tile
+constexpr int TILEB = TR * ROWB; // 16 KB
+constexpr float kLog2e = 1.4426950408889634f;
+
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+// Barrier without the fence of __syncthreads(): the caller's own global->LDS
+// loads are waited for explicitly (vmcnt 0), the barrier makes every wave's
+// loads visible and orders this step's reads before the next refill.
+__device__ __forceinline__ void barrier_loads_done(void) {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int tile_off(int r, int c) { return r * ROWB + ((c ^ swz(r & 15)) << 4); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);  // nearest even
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// bf16 operand from 8 score registers base .. base+7 of a 32x32 result: the
+// contraction slots of the other operand are ordered to match (see tr_offsets).
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  const u32x4 w = {pack_bf16(s[base], s[base + 1]), pack_bf16(s[base + 2], s[base + 3]),
+                   pack_bf16(s[base + 4], s[base + 5]), pack_bf16(s[base + 6], s[base + 7])};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// Row-operand offsets: row l32 (plus 32 * half as an immediate), chunk 2kc + hh.
+__device__ __forceinline__ void row_offsets(int l32, int hh, int (&off)[8]) {
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) off[kc] = tile_off(l32, 2 * kc + hh);
+}
+
+// Transposing-read offsets for an operand whose rows are the contraction
+// (rows 16mm + 8(e/4) + 4hh + e%4 in slot e) and whose m index is the channel
+// 32dt + l32.  ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives
+// element j%4 of the 8-byte rows that lanes j/4, j/4+4, j/4+8, j/4+12
+// address.  Lane p of a group addresses row base + p/4, channels
+// d0 + 4(p%4) .. +3, so lane j ends up with channel d0 + j of rows base..+3.
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[8]) {
+  const int hh = lane >> 5;
+  const int tr_row = 4 * hh + ((lane & 15) >> 2);
+  const int tr_ch = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int ch = 32 * dt + tr_ch;
+      off[2 * dt + q] = tile_off(tr_row + 8 * q, ch >> 3) + 2 * (ch & 7);
+    }
+}
+
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, const int (&off)[8], int dt,
+                                             int row0) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(tile + off[2 * dt] + row0 * ROWB));
+  const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(tile + off[2 * dt + 1] + row0 * ROWB));
+  const u32x4 w = {__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1],
+                   __builtin_bit_cast(u32x2, c)[0], __builtin_bit_cast(u32x2, c)[1]};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ bf16x8 row_operand(const unsigned char* tile, const int (&off)[8], int kc,
+                                              int row0) {
+  return *reinterpret_cast<const bf16x8*>(tile + off[kc] + row0 * ROWB);
+}
+
+// XCD-aware block order (workgroups are dealt round-robin to the 8 XCDs):
+// consecutive logical ids, which share a (batch, head), land on one XCD.
+__device__ __forceinline__ int logical_block(int nb) {
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int per = nb >> 3, extra = nb & 7;
+  return xcd * per + min(xcd, extra) + (bid >> 3);
+}
+
+// Stage one 64-row tile (rows row0.. of a [rows][stride] bf16 tensor, last
+// valid row `last`) into LDS with global->LDS loads: the wave issues `n`
+// 1-KB instructions starting at instruction i0; instruction i fills rows
+// 4i .. 4i+3, lane l slot l%16 of row 4i + l/16 with the chunk that the row's
+// swizzle puts there.
+__device__ __forceinline__ void stage_tile(const uint16_t* base, int64_t stride, int row0, int last,
+                                           unsigned char* tile, int i0, int n, int lane) {
+  for (int j = 0; j < n; ++j) {
+    const int i = i0 + j;
+    const int r = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r & 15);
+    const int grow = min(row0 + r, last);
+    const unsigned char* src = (const unsigned char*)(base + (int64_t)grow * stride) + c * 16;
+    __builtin_amdgcn_global_load_lds(src, (HV_LDS void*)(tile + i * 1024), 16, 0, 0);
+  }
+}
+
+// 64 consecutive fp32 values (rows row0.., clamped to `last`) of a row vector.
+__device__ __forceinline__ void stage_vec(const float* base, int row0, int last, float* dst,
+                                          int lane) {
+  const float* src = base + min(row0 + lane, last);
+  __builtin_amdgcn_global_load_lds(src, (HV_LDS void*)dst, 4, 0, 0);
+}
+
+// ---------------------------------------------------------------- delta ----
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int chunk = (int)(gid & 15);
+  const int64_t row = gid >> 4;  // b * seq_len + n
+  if (row >= (int64_t)p.batch * p.seq_len) return;  // whole 16-lane rows leave together
+  const int b = (int)(row / p.seq_len);
+  const int n = (int)(row - (int64_t)b * p.seq_len);
+  const int64_t base = (int64_t)b * p.stride_b + (int64_t)n * p.stride_l + chunk * 8;
+  const u32x4* op = reinterpret_cast<const u32x4*>(p.o + base);
+  const u32x4* gp = reinterpret_cast<const u32x4*>(p.dout + base);
+#pragma unroll
+  for (int h0 = 0; h0 < HV_HEADS; h0 += 8) {
+    u32x4 ov[8], gv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ov[i] = op[(h0 + i) * 16];
+      gv[i] = gp[(h0 + i) * 16];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s = fmaf(__uint_as_float(ov[i][j] << 16), __uint_as_float(gv[i][j] << 16), s);
+        s = fmaf(__uint_as_float(ov[i][j] & 0xffff0000u), __uint_as_float(gv[i][j] & 0xffff0000u), s);
+      }
+      s = row16_sum(s);
+      if (chunk == 0) p.delta[((int64_t)b * HV_HEADS + h0 + i) * p.seq_len + n] = s;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- dK, dV --
+constexpr int KV_WAVES = 4;
+constexpr int KV_KEYS = KV_WAVES * 32;  // keys per workgroup
+
+__global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sQ0[TILEB], sQ1[TILEB], sG0[TILEB], sG1[TILEB];
+  __shared__ __attribute__((aligned(16))) float sL0[TR], sL1[TR], sD0[TR], sD1[TR];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto qbuf = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return sQ0; else return sQ1; };
+  auto gbuf = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return sG0; else return sG1; };
+  auto lbuf = [&](auto st) -> float* { if constexpr (decltype(st)::value == 0) return sL0; else return sL1; };
+  auto dbuf = [&](auto st) -> float* { if constexpr (decltype(st)::value == 0) return sD0; else return sD1; };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int logical = logical_block(p.n_kv_blocks);
+  const int kb = logical % p.n_kblocks;
+  const int bh = logical / p.n_kblocks;
+  const int head = bh % HV_HEADS;
+  const int b = bh / HV_HEADS;
+  const int L = p.seq_len;
+  const int Lk = p.lk[b];
+  const int64_t sl = p.stride_l;
+  const int64_t hbase = (int64_t)b * p.stride_b + (int64_t)head * D;
+  const int64_t vbase = ((int64_t)b * HV_HEADS + head) * L;  // lse / delta row 0
+
+  // K and V of this lane's key as the B operands (n = key, k = channels
+  // 16kc + 8hh .. +7); keys past the valid ones read the last valid row and
+  // are masked out of P and dS below.
+  const int key = kb * KV_KEYS + wave * 32 + l32;
+  const bool key_ok = key < Lk;
+  bf16x8 kf[8], vf[8];
+  {
+    const int64_t r = hbase + (int64_t)min(key, Lk - 1) * sl + hh * 8;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      kf[kc] = *reinterpret_cast<const bf16x8*>(p.k + r + kc * 16);
+      vf[kc] = *reinterpret_cast<const bf16x8*>(p.v + r + kc * 16);
+    }
+  }
+  int roff[8], troff[8];
+  row_offsets(l32, hh, roff);
+  tr_offsets(lane, troff);
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dk[dt][v] = dv[dt][v] = 0.f;
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float c2 = p.scale_log2;
+  // a block of padded keys only has zero gradients: skip the query loop
+  const int nq = kb * KV_KEYS >= Lk ? 0 : (L + TR - 1) / TR;
+
+  // 16 instructions per 64-row tile and tensor: wave w issues 4w .. 4w+3
+  auto load = [&](auto st, int t) {
+    stage_tile(p.q + hbase, sl, t * TR, L - 1, qbuf(st), 4 * wave, 4, lane);
+    stage_tile(p.dout + hbase, sl, t * TR, L - 1, gbuf(st), 4 * wave, 4, lane);
+    if (wave == 0) stage_vec(p.lse + vbase, t * TR, L - 1, lbuf(st), lane);
+    if (wave == 1) stage_vec(p.delta + vbase, t * TR, L - 1, dbuf(st), lane);
+  };
+
+  auto tile = [&](auto st, int t) {
+    const unsigned char* qt = qbuf(st);
+    const unsigned char* gt = gbuf(st);
+    const float* lt = lbuf(st);
+    const float* dtv = dbuf(st);
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+      f32x16 s = zero16, dp = zero16;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 32 * qh), kf[kc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 32 * qh), vf[kc], dp, 0, 0, 0);
+      }
+      // rows of register v: query 32qh + 8(v/4) + 4hh + v%4 of the tile
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = 32 * qh + 8 * g + 4 * hh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + r);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dtv + r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g + e;
+          const bool ok = key_ok && (t * TR + r + e < L);
+          const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l4[e] * kLog2e)) : 0.f;
+          s[v] = pv;
+          dp[v] = ok ? pv * (dp[v] - d4[e]) : 0.f;
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        const bf16x8 pb = pack8(s, 8 * mm);
+        const bf16x8 db = pack8(dp, 8 * mm);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(gt, troff, dt, 32 * qh + 16 * mm), pb, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, troff, dt, 32 * qh + 16 * mm), db, dk[dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nq > 0) load(I0{}, 0);
+  int t = 0;
+  for (; t + 2 <= nq; t += 2) {
+    barrier_loads_done();
+    load(I1{}, t + 1);
+    tile(I0{}, t);
+    barrier_loads_done();
+    if (t + 2 < nq) load(I0{}, t + 2);
+    tile(I1{}, t + 1);
+  }
+  if (t < nq) {
+    barrier_loads_done();
+    tile(I0{}, t);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+  // lane owns key `key`, channels 32dt + 8j + 4hh .. +3 (register 4j .. 4j+3)
+  if (key < L) {
+    const float sc = p.scale;
+    uint16_t* kp = p.dk + hbase + (int64_t)key * sl;
+    uint16_t* vp = p.dv + hbase + (int64_t)key * sl;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 wk, wv;
+        wk.x = pack_bf16(dk[dt][4 * j] * sc, dk[dt][4 * j + 1] * sc);
+        wk.y = pack_bf16(dk[dt][4 * j + 2] * sc, dk[dt][4 * j + 3] * sc);
+        wv.x = pack_bf16(dv[dt][4 * j], dv[dt][4 * j + 1]);
+        wv.y = pack_bf16(dv[dt][4 * j + 2], dv[dt][4 * j + 3]);
+        *reinterpret_cast<u32x2*>(kp + dt * 32 + 8 * j + 4 * hh) = wk;
+        *reinterpret_cast<u32x2*>(vp + dt * 32 + 8 * j + 4 * hh) = wv;
+      }
+  }
+}
+
+// --------------------------------------------------------------------- dQ --
+constexpr int Q_WAVES = 4;
+constexpr int Q_ROWS = Q_WAVES * 32;  // queries per workgroup
+
+__global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sK0[TILEB], sK1[TILEB], sV0[TILEB], sV1[TILEB];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto kbuf = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return sK0; else return sK1; };
+  auto vbuf = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return sV0; else return sV1; };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int logical = logical_block(p.n_q_blocks);
+  const int qb = logical % p.n_qblocks;
+  const int bh = logical / p.n_qblocks;
+  const int head = bh % HV_HEADS;
+  const int b = bh / HV_HEADS;
+  const int L = p.seq_len;
+  const int Lk = p.lk[b];
+  const int64_t sl = p.stride_l;
+  const int64_t hbase = (int64_t)b * p.stride_b + (int64_t)head * D;
+  const int64_t vbase = ((int64_t)b * HV_HEADS + head) * L;
+
+  // Q and dO of this lane's query as B operands (n = query, k = channels)
+  const int q0 = qb * Q_ROWS + wave * 32;
+  const int qrow = min(q0 + l32, L - 1);  // rows past the end are computed, never stored
+  bf16x8 qf[8], gf[8];
+  {
+    const int64_t r = hbase + (int64_t)qrow * sl + hh * 8;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      qf[kc] = *reinterpret_cast<const bf16x8*>(p.q + r + kc * 16);
+      gf[kc] = *reinterpret_cast<const bf16x8*>(p.dout + r + kc * 16);
+    }
+  }
+  const float lse2 = p.lse[vbase + qrow] * kLog2e;
+  const float dlt = p.delta[vbase + qrow];
+  int roff[8], troff[8];
+  row_offsets(l32, hh, roff);
+  tr_offsets(lane, troff);
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dq[dt][v] = 0.f;
+  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float c2 = p.scale_log2;
+  const int nk = (Lk + TR - 1) / TR;
+
+  // 16 instructions per tile and tensor, split evenly over the waves
+  constexpr int per_wave = 16 / Q_WAVES;
+  auto load = [&](auto st, int t) {
+    stage_tile(p.k + hbase, sl, t * TR, Lk - 1, kbuf(st), per_wave * wave, per_wave, lane);
+    stage_tile(p.v + hbase, sl, t * TR, Lk - 1, vbuf(st), per_wave * wave, per_wave, lane);
+  };
+
+  auto tile = [&](auto st, int t) {
+    const unsigned char* kt = kbuf(st);
+    const unsigned char* vt = vbuf(st);
+    // S^T = K Q^T and dP^T = V dO^T: 64 keys (two halves) x this wave's 32 queries
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) { s[h] = zero16; dp[h] = zero16; }
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, roff, kc, 32 * h), qf[kc], s[h], 0, 0, 0);
+        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, roff, kc, 32 * h), gf[kc], dp[h], 0, 0, 0);
+      }
+    // key of register v in half h: 32h + 8(v/4) + 4hh + v%4
+    const int lim = Lk - t * TR;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool ok = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3) < lim;
+        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[h][v], c2, -lse2)) : 0.f;
+        s[h][v] = ok ? pv * (dp[h][v] - dlt) : 0.f;  // dS^T
+      }
+    // dQ^T += K^T dS^T, keys in groups of 16
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const bf16x8 db = pack8(s[mm >> 1], 8 * (mm & 1));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, troff, dt, 16 * mm), db, dq[dt], 0, 0, 0);
+    }
+  };
+
+  load(I0{}, 0);
+  int t = 0;
+  for (; t + 2 <= nk; t += 2) {
+    barrier_loads_done();
+    load(I1{}, t + 1);
+    tile(I0{}, t);
+    barrier_loads_done();
+    if (t + 2 < nk) load(I0{}, t + 2);
+    tile(I1{}, t + 1);
+  }
+  if (t < nk) {
+    barrier_loads_done();
+    tile(I0{}, t);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+
+  const int orow = q0 + l32;
+  if (orow < L) {
+    const float sc = p.scale;
+    uint16_t* op = p.dq + hbase + (int64_t)orow * sl;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w.x = pack_bf16(dq[dt][4 * j] * sc, dq[dt][4 * j + 1] * sc);
+        w.y = pack_bf16(dq[dt][4 * j + 2] * sc, dq[dt][4 * j + 3] * sc);
+        *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * j + 4 * hh) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(BwdParams& p, hipStream_t stream) {
+  p.n_qblocks = (p.seq_len + Q_ROWS - 1) / Q_ROWS;
+  p.n_kblocks = (p.seq_len + KV_KEYS - 1) / KV_KEYS;
+  p.n_q_blocks = p.batch * HV_HEADS * p.n_qblocks;
+  p.n_kv_blocks = p.batch * HV_HEADS * p.n_kblocks;
+  const int64_t threads = (int64_t)p.batch * p.seq_len * 16;
+  hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)p.n_kv_blocks), dim3(KV_WAVES * 64), 0,
+                     stream, p);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)p.n_q_blocks), dim3(Q_WAVES * 64), 0, stream,
+                     p);
+  return hipGetLastError();
+}
+
+}  // namespace hv

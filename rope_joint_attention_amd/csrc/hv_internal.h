@@ -113,4 +113,31 @@ struct MergeParams {
 
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t stream);
 
+// ---- attention backward -----------------------------------------------------
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;    // [batch][24][seq_len], natural log
+  float* delta;        // [batch][24][seq_len], written by the first kernel
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int64_t stride_b;    // elements, shared by all bf16 tensors
+  int64_t stride_l;
+  int32_t batch;
+  int32_t seq_len;
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e)
+  int32_t n_qblocks;   // query blocks per (batch, head) of the dq kernel
+  int32_t n_kblocks;   // key blocks per (batch, head) of the dkdv kernel
+  int32_t n_q_blocks;  // dq workgroups
+  int32_t n_kv_blocks; // dkdv workgroups
+  int32_t lk[HV_MAX_BATCH];  // valid keys per batch entry
+};
+
+hipError_t launch_attn_bwd(BwdParams& p, hipStream_t stream);
+
 }  // namespace hv

@@ -355,6 +355,67 @@ int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_b
   return e == hipSuccess ? HV_OK : HV_ERR_HIP;
 }
 
+int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                           const hv_bf16* out, const hv_bf16* dout, const float* lse,
+                           const int32_t* text_valid_len, int64_t n_video, hv_bf16* dq,
+                           hv_bf16* dk, hv_bf16* dv, float* delta, const hv_layout* layout,
+                           float softmax_scale, void* stream) {
+  int64_t extent = 0;
+  int st = check_layout(layout, &extent);
+  if (st != HV_OK) return st;
+  if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
+  const hv_bf16* ins[5] = {q, k, v, out, dout};
+  hv_bf16* outs[3] = {dq, dk, dv};
+  for (const hv_bf16* t : ins)
+    if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
+  for (const hv_bf16* t : outs)
+    if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
+  if (!lse || !delta || ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)delta & 3u) != 0)
+    return HV_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i) {
+    for (const hv_bf16* t : ins)
+      if (overlap(outs[i], t, layout, extent)) return HV_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j], layout, extent)) return HV_ERR_INVALID_ARG;
+  }
+  const uintptr_t vb = (uintptr_t)layout->batch * HV_HEADS * layout->seq_len * sizeof(float);
+  const uintptr_t tb = (uintptr_t)extent * sizeof(hv_bf16);
+  if (ranges_meet(delta, vb, lse, vb)) return HV_ERR_INVALID_ARG;
+  for (const hv_bf16* t : ins)
+    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
+  for (const hv_bf16* t : outs)
+    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
+  if (layout->batch == 0 || layout->seq_len == 0) return HV_OK;
+
+  hv::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  const int64_t text_cap = layout->seq_len - n_video;
+  for (int b = 0; b < layout->batch; ++b) {
+    const int64_t valid = text_valid_len ? text_valid_len[b] : text_cap;
+    if (valid < 0 || valid > text_cap) return HV_ERR_INVALID_ARG;
+    if (n_video + valid < 1) return HV_ERR_INVALID_ARG;
+    p.lk[b] = (int32_t)(n_video + valid);
+  }
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.stride_b = layout->stride_b;
+  p.stride_l = layout->stride_l;
+  p.batch = layout->batch;
+  p.seq_len = layout->seq_len;
+  p.scale_log2 = scale_log2(softmax_scale);
+  p.scale = (float)((double)p.scale_log2 / 1.4426950408889634);
+  const hipError_t e = hv::launch_attn_bwd(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
 int hv_attention_merge(const hv_bf16* const* outs, const float* const* lses, int32_t n_parts,
                        hv_bf16* out, float* lse_out, const hv_layout* layout, void* stream) {
   int64_t extent = 0;

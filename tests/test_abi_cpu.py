@@ -349,3 +349,37 @@ def test_varlen_empty_segments_are_valid():
     # all-empty segments: nothing to launch
     assert varlen(cq=(0, 0, 0), ck=(0, 0, 5)) == hv.HV_OK
     assert varlen(cq=(0, 0), ck=(0, 0), lay=layout(seq=0, sb=0)) == hv.HV_OK
+
+
+# ------------------------------------------------------------ backward
+def bwd(q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP, o=FAKE + 3 * SEP, g=FAKE + 4 * SEP, lse=LSE,
+        valid=(10,), n_video=40, dq=FAKE + 10 * SEP, dk=FAKE + 11 * SEP, dv=FAKE + 12 * SEP,
+        delta=FAKE + 13 * SEP, lay=None):
+    lib = hv.load_library()
+    lay = layout() if lay is None else lay
+    arr = None if valid is None else (ctypes.c_int32 * max(1, len(valid)))(*valid)
+    return lib.hv_joint_attention_bwd(q, k, v, o, g, lse, arr, n_video, dq, dk, dv, delta,
+                                      ctypes.byref(lay) if lay is not False else None, 0.0, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(k=0), E), (dict(v=0), E), (dict(o=0), E), (dict(g=0), E),
+    (dict(lse=0), E), (dict(dq=0), E), (dict(dk=0), E), (dict(dv=0), E), (dict(delta=0), E),
+    (dict(lay=False), E), (dict(dq=FAKE + 10 * SEP + 2), E), (dict(lse=LSE + 1), E),
+    (dict(delta=FAKE + 13 * SEP + 2), E),
+    (dict(dq=FAKE + 100 * 3072 * 2), E),                  # dq inside q
+    (dict(dk=FAKE + 10 * SEP + 64 * 3072 * 2), E),        # dk inside dq
+    (dict(dv=FAKE + 4 * SEP), E),                         # dv is dout
+    (dict(delta=LSE + 64), E),                            # delta inside lse
+    (dict(delta=FAKE + 12 * SEP + 128), E),               # delta inside dv
+    (dict(lse=FAKE + 2 * SEP + 256), E),                  # lse inside v
+    (dict(valid=(-1,)), E), (dict(valid=(261,)), E), (dict(n_video=0, valid=(0,)), E),
+    (dict(n_video=301), E),
+    (dict(lay=layout(heads=8)), U), (dict(lay=layout(batch=65), valid=None), U),
+])
+def test_backward_validation(kwargs, expect):
+    assert bwd(**kwargs) == expect
+
+
+def test_backward_empty_call():
+    assert bwd(lay=layout(batch=0), valid=None, n_video=0) == hv.HV_OK

@@ -1,0 +1,152 @@
+"""GPU parity of hv_joint_attention_bwd (dQ, dK, dV) against the fp64 oracle,
+through the C ABI.
+
+The forward runs on the GPU first (hv_attention_fwd_lse gives out and the
+log-sum-exp the backward consumes); the oracle computes the gradients from
+the same bf16 q, k, v, dout in fp64.  Gates, per gradient: relative Frobenius
+error <= 1e-2, max-abs error <= 2e-2 * max|ref|, mean-abs <= 2e-3 * max|ref|,
+no NaN/Inf; the kernel rounds P and dS to bf16 as MFMA operands (2^-9
+relative each, averaging out) and reads O in bf16, so a correct kernel sits
+near 2e-3 relative.  Sizes are floored at 1e-3 per element, so an exactly-zero
+reference gradient (a single key) is held to rounding noise below 2e-5.
+Padded keys must get exactly zero dK, dV.
+"""
+import numpy as np
+import pytest
+
+import hvinputs
+from hvtest_util import bits_to_torch, log, torch_to_bits, widen
+from oracle import joint_attention_bwd, joint_attention_bwd_dq_rows, token_grid
+
+pytestmark = pytest.mark.gpu
+
+
+def grad_close(got, ref, what, floor=1e-3):
+    # errors are measured against the reference's size, but never against less
+    # than `floor` per element: a gradient that is exactly zero (one key: dS = 0)
+    # comes out of fp32 as rounding noise of the cancelling dP - D
+    d = np.abs(got - ref)
+    scale = max(float(np.abs(ref).max()), floor)
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), floor * np.sqrt(ref.size)))
+    e = {"rel_fro": rel, "max_rel": float(d.max()) / scale, "mean_rel": float(d.mean()) / scale}
+    assert np.isfinite(got).all(), what
+    assert rel <= 1e-2 and e["max_rel"] <= 2e-2 and e["mean_rel"] <= 2e-3, f"{what}: {e}"
+    return e
+
+
+def run_bwd(bits, dout_bits, n_video, valid, scale=None, fused=False):
+    import torch
+    import rope_joint_attention_amd as hv
+
+    if fused:
+        B, L = bits["q"].shape[:2]
+        buf = torch.zeros((B, L, 3, 24, 128), dtype=torch.bfloat16, device="cuda")
+        for i, n in enumerate("qkv"):
+            buf[:, :, i] = bits_to_torch(bits[n])
+        q, k, v = buf[:, :, 0], buf[:, :, 1], buf[:, :, 2]
+    else:
+        q, k, v = (bits_to_torch(bits[n]) for n in "qkv")
+    lk = [n_video + x for x in valid]
+    out, lse = hv.hv_attention_fwd_lse(q, k, v, lk, softmax_scale=scale)
+    g = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    g.copy_(bits_to_torch(dout_bits))
+    dq, dk, dv = hv.hv_joint_attention_bwd(q, k, v, out, g, lse, list(valid), n_video,
+                                           softmax_scale=scale)
+    torch.cuda.synchronize()
+    return torch_to_bits(dq), torch_to_bits(dk), torch_to_bits(dv)
+
+
+def draw(B, L, seed, q_scale=1.0):
+    bits = hvinputs.draw_qkv(B, L, seed, q_scale=q_scale)
+    dout = hvinputs.draw_qkv(B, L, seed + 7919)["q"]
+    return bits, dout
+
+
+@pytest.mark.parametrize("B,L,N,valid,scale,q_scale,fused", [
+    (1, 1, 1, (0,), None, 1.0, False),
+    (1, 40, 24, (10,), None, 1.0, False),
+    (2, 129, 100, (29, 3), None, 1.0, False),
+    (1, 300, 256, (44,), 0.05, 1.0, True),
+    (3, 257, 200, (0, 57, 20), None, 4.0, False),   # peaky
+    (1, 700, 640, (60,), None, 1.0, False),         # several tiles and key blocks, ragged
+])
+def test_bwd_small(B, L, N, valid, scale, q_scale, fused):
+    bits, dout = draw(B, L, seed=L * 3 + N, q_scale=q_scale)
+    log(f"bwd small B={B} L={L} N={N} valid={valid} scale={scale} q_scale={q_scale} fused={fused}")
+    dq, dk, dv = run_bwd(bits, dout, N, valid, scale, fused)
+    ref = joint_attention_bwd(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), widen(dout), N,
+                              valid, scale=scale)
+    for name, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        e = grad_close(widen(got), r, name)
+        log(f"  {name} {e}")
+    for b in range(B):
+        n = N + valid[b]
+        assert not widen(dk[b, n:]).any() and not widen(dv[b, n:]).any()
+
+
+def test_bwd_poisoned_padding_and_determinism():
+    import torch
+
+    B, L, N, valid = 2, 200, 150, (20, 50)
+    bits, dout = draw(B, L, seed=5)
+    ref = run_bwd(bits, dout, N, valid)
+    poisoned = {n: bits[n].copy() for n in "qkv"}
+    nan = hvinputs.f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+    poisoned["k"][0, N + 20:] = nan
+    poisoned["v"][1, N + 50:] = nan
+    again = run_bwd(poisoned, dout, N, valid)
+    for a, b in zip(ref, again):
+        assert np.array_equal(a, b)
+    twice = run_bwd(bits, dout, N, valid)
+    for a, b in zip(ref, twice):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.timeout(600)
+def test_bwd_image_workload_full():
+    wl = hvinputs.WORKLOADS["image_256x256"]
+    g = token_grid(wl.frames, wl.height, wl.width)
+    L = g.n_video + wl.text_capacity
+    bits, dout = draw(wl.batch, L, wl.seed)
+    log(f"bwd image workload L={L}")
+    dq, dk, dv = run_bwd(bits, dout, g.n_video, wl.valid)
+    ref = joint_attention_bwd(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), widen(dout),
+                              g.n_video, wl.valid)
+    for name, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        log(f"  {name} {grad_close(widen(got), r, name)}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["video_544x960x17", "video_720x1280x33_b2", "video_544x960x129",
+                                  "video_720x1280x129"])
+def test_bwd_workloads(name):
+    # dQ on sampled rows against the oracle row by row; dK and dV on every row
+    # through identities that hold at any size (the key gradients of each
+    # (batch, head) sum to zero; the value gradients sum to the summed dO),
+    # plus all rows of two heads against the full oracle where it is cheap.
+    wl = hvinputs.WORKLOADS[name]
+    g = token_grid(wl.frames, wl.height, wl.width)
+    L = g.n_video + wl.text_capacity
+    bits, dout = draw(wl.batch, L, wl.seed)
+    log(f"bwd workload {name} B={wl.batch} L={L}")
+    dq, dk, dv = run_bwd(bits, dout, g.n_video, wl.valid)
+    rows = hvinputs.sample_rows(L, g.n_video, g.gh * g.gw, wl.seed, n_random=32, edge=8)
+    heads = [0, 13, 23]
+    ref = joint_attention_bwd_dq_rows(widen(bits["q"][:, rows]), widen(bits["k"]), widen(bits["v"]),
+                                      widen(dout[:, rows]), g.n_video, wl.valid, heads=heads)
+    log(f"  dq rows {grad_close(widen(dq[:, rows][:, :, heads]), ref, 'dq rows')}")
+    for b in range(wl.batch):
+        n = g.n_video + wl.valid[b]
+        dkb = widen(dk[b, :n]).sum(axis=0)              # [24, 128]
+        scale_k = np.abs(widen(dk[b, :n])).sum(axis=0)
+        assert np.all(np.abs(dkb) <= 2e-2 * scale_k + 1e-6), float((np.abs(dkb) / scale_k).max())
+        dvb = widen(dv[b, :n]).sum(axis=0)
+        gsum = widen(dout[b]).sum(axis=0)
+        err = np.abs(dvb - gsum)
+        assert np.all(err <= 1e-2 * np.abs(widen(dv[b, :n])).sum(axis=0) + 1e-3), float(err.max())
+        assert not widen(dk[b, n:]).any() and not widen(dv[b, n:]).any()
+    if L <= 11000:
+        full = joint_attention_bwd(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), widen(dout),
+                                   g.n_video, wl.valid, heads=[0, 13])
+        for i, (nm, got) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+            log(f"  {nm} heads 0,13 {grad_close(widen(got[:, :, [0, 13]]), full[i], nm)}")

@@ -98,3 +98,13 @@ def test_one_key_closed_form():
     assert np.allclose(dq, 0, atol=1e-13) and np.allclose(dk, 0, atol=1e-13)
     assert np.allclose(dv[0, 0], g[0].sum(axis=0), rtol=1e-13, atol=1e-13)
     assert not dv[0, 1:].any()
+
+
+def test_dq_rows_matches_the_full_gradient():
+    from oracle import joint_attention_bwd_dq_rows
+
+    q, k, v, g, N, valid = setup(9, B=2, L=14, N=10, valid=(1, 4))
+    dq, _, _ = joint_attention_bwd(q, k, v, g, N, valid)
+    rows = np.array([0, 3, 10, 13])
+    sub = joint_attention_bwd_dq_rows(q[:, rows], k, v, g[:, rows], N, valid)
+    assert np.allclose(sub, dq[:, rows], rtol=1e-13, atol=1e-14)
