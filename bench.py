@@ -17,8 +17,8 @@ sample of the same workload on the host cores.  The QK-norm + RoPE prologue
 (hv_qk_norm_rope3d_apply, all rows of q and k) is timed separately on the
 same resident tensors and reported beside the step (qknorm_rope_*).  The
 `extras` object times one rank's share of an 8-way ring attention (partial
-attention per K/V block plus the log-sum-exp merge) and a packed
-variable-length call (--no-extras skips them).
+attention per K/V block plus the log-sum-exp merge), a packed
+variable-length call and the attention backward (--no-extras skips them).
 """
 from __future__ import annotations
 
@@ -126,6 +126,10 @@ def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int)
     varlen_pack: the batch of two 720x1280x33 clips with 37 and 256 valid text
       tokens packed as [valid | padded tail] segments of one sequence (the
       padded tails attend to themselves), one hv_joint_attention_varlen_fwd.
+    backward: hv_joint_attention_bwd at this size.  `tflops` counts the usual
+      five matrix products of an attention backward (2.5x the forward's
+      FLOPs); the kernels execute seven (S and dP are formed twice, once for
+      dK/dV and once for dQ), reported as `tflops_executed`.
     """
     out = {}
     P = 8
@@ -181,6 +185,22 @@ def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int)
         out["varlen_pack"] = {"workload": wb.name, "segments": len(cu) - 1, "rows": T,
                               "ms": round(ms_v, 4), "tflops": round(flv / (ms_v / 1e3) / 1e12, 2)}
         del op
+
+    # backward of the headline attention: forward with log-sum-exp once, then
+    # the gradients for an upstream gradient (v's values stand in for dO)
+    lk = [grid.n_video + x for x in wl.valid]
+    o, lse = hv.hv_attention_fwd_lse(q, k, v, lk)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty_like(lse)
+    ms_b = timed(torch, stream, lambda: hv.hv_joint_attention_bwd(
+        q, k, v, o, v, lse, list(wl.valid), grid.n_video, dq=dq, dk=dk, dv=dv, delta=delta),
+        max(2, reps // 2))
+    fwd_fl = 4.0 * HEADS * HEAD_DIM * L * sum(lk)
+    out["backward"] = {"ms": round(ms_b, 4),
+                       "tflops": round(2.5 * fwd_fl / (ms_b / 1e3) / 1e12, 2),
+                       "flops_counted": 2.5 * fwd_fl,
+                       "tflops_executed": round(3.5 * fwd_fl / (ms_b / 1e3) / 1e12, 2)}
+    del o, lse, dq, dk, dv, delta
     return out
 
 
