@@ -18,9 +18,11 @@
 //            K and V of its keys held in registers as MFMA operands; it walks
 //            all query tiles of 64 rows (Q, dO, lse, D staged in LDS by
 //            global->LDS loads, two stages) and accumulates dV^T += dO^T P and
-//            dK^T += Q^T dS in registers;
-//   * dq:    one workgroup per (batch, head, 128 queries), 4 waves of 32
-//            queries with Q and dO in registers; it walks the key tiles of 64
+//            dK^T += Q^T dS in registers; the two 32-query units of a tile
+//            are staggered so one unit's exp/dS work runs under the other's
+//            MFMAs;
+//   * dq:    one workgroup per (batch, head, 256 queries), 8 waves of 32
+//            queries (two per SIMD) with Q and dO in registers; it walks the key tiles of 64
 //            rows (K, V staged the same way) and accumulates dQ^T += K^T dS^T.
 // dQ is computed in its own pass (recomputing S and dP) instead of by atomics
 // from the key-block kernel: no fp32 scratch, deterministic results.
@@ -270,46 +272,73 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     if (wave == 1) stage_vec(p.delta + vbase, t * TR, L - 1, dbuf(st), lane);
   };
 
+  // One 64-query tile in two units of 32 queries.  Per unit: S = Q K^T and
+  // dP = dO V^T (16 MFMAs), then P and dS (VALU), then dV^T += dO^T P and
+  // dK^T += Q^T dS (16 MFMAs).  The units are staggered so that the VALU work
+  // of one runs under the MFMAs of the other:
+  //   A0 | A1 + V0 | B0 + V1 | B1
   auto tile = [&](auto st, int t) {
     const unsigned char* qt = qbuf(st);
     const unsigned char* gt = gbuf(st);
     const float* lt = lbuf(st);
     const float* dtv = dbuf(st);
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-      f32x16 s = zero16, dp = zero16;
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 32 * qh), kf[kc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 32 * qh), vf[kc], dp, 0, 0, 0);
-      }
-      // rows of register v: query 32qh + 8(v/4) + 4hh + v%4 of the tile
+    f32x16 s0 = zero16, d0 = zero16, s1 = zero16, d1 = zero16;
+    f32x4 l4[2][4], d4[2][4];
+    // rows of register v of unit u: query 32u + 8(v/4) + 4hh + v%4 of the tile
+    auto stats = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int r = 32 * qh + 8 * g + 4 * hh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + r);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dtv + r);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g + e;
-          const bool ok = key_ok && (t * TR + r + e < L);
-          const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[v], c2, -l4[e] * kLog2e)) : 0.f;
-          s[v] = pv;
-          dp[v] = ok ? pv * (dp[v] - d4[e]) : 0.f;
-        }
+        const int r = 32 * u + 8 * g + 4 * hh;
+        l4[u][g] = *reinterpret_cast<const f32x4*>(lt + r) * kLog2e;
+        d4[u][g] = *reinterpret_cast<const f32x4*>(dtv + r);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
+    };
+    auto grad = [&](f32x16& sv, f32x16& dv_, int u, int v) __attribute__((always_inline)) {
+      const int r = 32 * u + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const bool ok = key_ok && (t * TR + r < L);
+      const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(sv[v], c2, -l4[u][v >> 2][v & 3])) : 0.f;
+      sv[v] = pv;
+      dv_[v] = ok ? pv * (dv_[v] - d4[u][v >> 2][v & 3]) : 0.f;
+    };
+    // A0
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        const bf16x8 pb = pack8(s, 8 * mm);
-        const bf16x8 db = pack8(dp, 8 * mm);
+    for (int kc = 0; kc < 8; ++kc) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 0), kf[kc], s0, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 0), vf[kc], d0, 0, 0, 0);
+    }
+    stats(0);
+    // A1 + V0
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(gt, troff, dt, 32 * qh + 16 * mm), pb, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, troff, dt, 32 * qh + 16 * mm), db, dk[dt], 0, 0, 0);
-        }
-      }
+    for (int kc = 0; kc < 8; ++kc) {
+      __builtin_amdgcn_sched_barrier(0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 32), kf[kc], s1, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 32), vf[kc], d1, 0, 0, 0);
+      grad(s0, d0, 0, 2 * kc);
+      grad(s0, d0, 0, 2 * kc + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 pb0[2] = {pack8(s0, 0), pack8(s0, 8)};
+    const bf16x8 db0[2] = {pack8(d0, 0), pack8(d0, 8)};
+    stats(1);
+    // B0 + V1
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int mm = j >> 2, dt = j & 3;
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(gt, troff, dt, 16 * mm), pb0[mm], dv[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, troff, dt, 16 * mm), db0[mm], dk[dt], 0, 0, 0);
+      grad(s1, d1, 1, 2 * j);
+      grad(s1, d1, 1, 2 * j + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 pb1[2] = {pack8(s1, 0), pack8(s1, 8)};
+    const bf16x8 db1[2] = {pack8(d1, 0), pack8(d1, 8)};
+    // B1
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int mm = j >> 2, dt = j & 3;
+      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(gt, troff, dt, 32 + 16 * mm), pb1[mm], dv[dt], 0, 0, 0);
+      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, troff, dt, 32 + 16 * mm), db1[mm], dk[dt], 0, 0, 0);
     }
   };
 
@@ -350,7 +379,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
 }
 
 // --------------------------------------------------------------------- dQ --
-constexpr int Q_WAVES = 4;
+constexpr int Q_WAVES = 8;
 constexpr int Q_ROWS = Q_WAVES * 32;  // queries per workgroup
 
 __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams p) {
@@ -413,34 +442,33 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
   auto tile = [&](auto st, int t) {
     const unsigned char* kt = kbuf(st);
     const unsigned char* vt = vbuf(st);
-    // S^T = K Q^T and dP^T = V dO^T: 64 keys (two halves) x this wave's 32 queries
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) { s[h] = zero16; dp[h] = zero16; }
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, roff, kc, 32 * h), qf[kc], s[h], 0, 0, 0);
-        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, roff, kc, 32 * h), gf[kc], dp[h], 0, 0, 0);
-      }
-    // key of register v in half h: 32h + 8(v/4) + 4hh + v%4
     const int lim = Lk - t * TR;
+    // two halves of 32 keys, one after the other (keeps the wave within 256
+    // registers, so two waves share each SIMD)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
+      f32x16 s = zero16, dp = zero16;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, roff, kc, 32 * h), qf[kc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, roff, kc, 32 * h), gf[kc], dp, 0, 0, 0);
+      }
+      // key of register v: 32h + 8(v/4) + 4hh + v%4
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const bool ok = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3) < lim;
-        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[h][v], c2, -lse2)) : 0.f;
-        s[h][v] = ok ? pv * (dp[h][v] - dlt) : 0.f;  // dS^T
+        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[v], c2, -lse2)) : 0.f;
+        s[v] = ok ? pv * (dp[v] - dlt) : 0.f;  // dS^T
       }
-    // dQ^T += K^T dS^T, keys in groups of 16
+      // dQ^T += K^T dS^T, keys in groups of 16
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const bf16x8 db = pack8(s[mm >> 1], 8 * (mm & 1));
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const bf16x8 db = pack8(s, 8 * m2);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, troff, dt, 16 * mm), db, dq[dt], 0, 0, 0);
+        for (int dt = 0; dt < 4; ++dt)
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, troff, dt, 32 * h + 16 * m2), db, dq[dt], 0, 0, 0);
+      }
     }
   };
 

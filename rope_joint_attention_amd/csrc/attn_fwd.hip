@@ -185,6 +185,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  // Waves w and w+4 share a SIMD.  Fixed, unequal priorities let one of the
+  // pair issue first whenever both are ready, so the other fills its stalls
+  // instead of the two advancing in lockstep (measured: about 0.5 % faster).
+  if (wave < 4) __builtin_amdgcn_s_setprio(2);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
