@@ -304,6 +304,14 @@ def main() -> int:
     qkn_ms = [e[0].elapsed_time(e[1]) for e in pev]
     progress(f"timed {args.steps} QK-norm + RoPE prologue calls")
 
+    # context for the HBM-bound kernels: a plain device-to-device copy of
+    # 1 GiB (torch's copy kernel), read + write bytes over its event time
+    csrc = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    copy_ms = timed(torch, stream, lambda: cdst.copy_(csrc), 5)
+    copy_gbps = 2.0 * csrc.numel() * 4 / (copy_ms / 1000.0) / 1e9
+    del csrc, cdst
+
     if args.copy_ref_mib > 0:
         n = args.copy_ref_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -352,6 +360,7 @@ def main() -> int:
         "qknorm_rope_ms_per_call": round(qkn_avg, 4),
         "qknorm_rope_GBps": round(qkn_gbps, 1),
         "qknorm_rope_pct_hbm_peak": round(100.0 * qkn_gbps / PEAK_HBM_GBPS, 2),
+        "hbm_copy_GBps": round(copy_gbps, 1),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),

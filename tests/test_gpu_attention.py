@@ -47,6 +47,7 @@ SMALL = [
     (1, 900, 124, [100]),      # L = 1024
     (3, 1500, 37, [37, 0, 20]),
     (1, 2047, 256, [255]),
+    (64, 60, 10, [i % 11 for i in range(64)]),   # maximum batch, every valid length 0..10
 ]
 
 

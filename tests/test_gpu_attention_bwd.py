@@ -150,3 +150,17 @@ def test_bwd_workloads(name):
                                    g.n_video, wl.valid, heads=[0, 13])
         for i, (nm, got) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
             log(f"  {nm} heads 0,13 {grad_close(widen(got[:, :, [0, 13]]), full[i], nm)}")
+
+
+def test_bwd_maximum_batch():
+    import rope_joint_attention_amd as hv
+
+    B, L, N = hv.HV_MAX_BATCH, 48, 40
+    valid = tuple(i % 9 for i in range(B))
+    bits, dout = draw(B, L, seed=6400)
+    log(f"bwd batch {B} L={L}")
+    dq, dk, dv = run_bwd(bits, dout, N, valid)
+    ref = joint_attention_bwd(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), widen(dout), N,
+                              valid, heads=[0, 7, 23])
+    for i, (name, got) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+        grad_close(widen(got[:, :, [0, 7, 23]]), ref[i], name)

@@ -172,3 +172,16 @@ def test_qknorm_then_attention_end_to_end(name):
     ref = joint_attention(qf, kf, widen(bits["v"]), g.n_video, wl.valid)
     e = assert_close(widen(ob[:, rows]), ref, f"{name} norm+rope+attention")
     log(f"  {e}")
+
+
+def test_qknorm_maximum_batch():
+    import rope_joint_attention_amd as hv
+
+    g = token_grid(5, 32, 48)
+    L = g.n_video + 3
+    B = hv.HV_MAX_BATCH
+    bits = hvinputs.draw_qkv(B, L, seed=646)
+    gam = hvinputs.draw_gamma(seed=647)
+    _, q2, k2 = run_qknorm(bits["q"], bits["k"], 5, 32, 48, 10000.0, gam, 1e-6)
+    check(bits["q"], q2, g, 10000.0, gam["q_video"], gam["q_text"], 1e-6)
+    check(bits["k"], k2, g, 10000.0, gam["k_video"], gam["k_text"], 1e-6)

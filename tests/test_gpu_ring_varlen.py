@@ -229,3 +229,45 @@ def test_varlen_padded_batch_matches_oracle():
             ref, _ = attention_lse(widen(flat["q"][None, tail]), widen(flat["k"][None, tail]),
                                    widen(flat["v"][None, tail]), [tail.size])
             assert_close(widen(ob[tail]), ref[0], f"entry {b} padded tail")
+
+
+def test_varlen_maximum_segment_count():
+    # HV_MAX_SEGMENTS packed segments of ragged lengths, some empty
+    import torch
+    import rope_joint_attention_amd as hv
+
+    r = np.random.default_rng(64)
+    lens = [int(x) for x in r.integers(0, 40, size=hv.HV_MAX_SEGMENTS)]
+    lens[5] = 0
+    lens[-1] = 1
+    cu = [0] + list(np.cumsum(lens))
+    T = cu[-1]
+    bits = hvinputs.draw_qkv(1, T, seed=6464)
+    log(f"varlen {len(lens)} segments T={T}")
+    q, k, v = (bits_to_torch(bits[n])[0] for n in "qkv")
+    out, lse = hv.hv_joint_attention_varlen_fwd(q, k, v, cu, want_lse=True)
+    torch.cuda.synchronize()
+    ref, lref = varlen_attention(widen(bits["q"][0]), widen(bits["k"][0]), widen(bits["v"][0]), cu, cu)
+    assert_close(widen(torch_to_bits(out)), ref, "varlen 64 segments")
+    lse_close(lse.cpu().numpy(), lref, "varlen 64 segments")
+
+
+def test_merge_maximum_part_count():
+    import torch
+    import rope_joint_attention_amd as hv
+
+    Lq, Lk, P = 130, 1600, hv.HV_MAX_MERGE_PARTS
+    bits = hvinputs.draw_qkv(2, Lk, seed=1616)
+    qb, kb, vb = bits["q"][:, :Lq], bits["k"], bits["v"]
+    q, k, v = bits_to_torch(qb), bits_to_torch(kb), bits_to_torch(vb)
+    bounds = [int(x) for x in np.linspace(0, Lk, P + 1)]
+    outs, lses = [], []
+    for a, b in zip(bounds, bounds[1:]):
+        o, l = hv.hv_attention_fwd_lse(q, k[:, a:b], v[:, a:b])
+        outs.append(o)
+        lses.append(l)
+    out, lse = hv.hv_attention_merge(outs, lses)
+    torch.cuda.synchronize()
+    ref, lref = attention_lse(widen(qb), widen(kb), widen(vb), [Lk, Lk])
+    assert_close(widen(torch_to_bits(out)), ref, "merge of 16 parts")
+    lse_close(lse.cpu().numpy(), lref, "merge of 16 parts")
