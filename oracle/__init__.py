@@ -30,7 +30,8 @@ Each function restates, in NumPy float64, what the HunyuanVideo notes page
 * ``joint_attention_bwd`` gradients dQ, dK, dV of the joint attention (the
                       report summary page's training-side attention cost),
                       by the chain rule through the softmax
-                      (``joint_attention_bwd_dq_rows``: dQ of selected rows);
+                      (``joint_attention_bwd_dq_rows``: dQ of selected rows;
+                      ``varlen_attention_bwd``: the same over packed segments);
 * ``hot_path``        token grid, RoPE and attention in sequence.
 
 Nothing here is blocked, fused or reordered beyond the formulas: the matrix
@@ -65,5 +66,6 @@ from .hv_oracle import (  # noqa: F401
     varlen_attention,
     joint_attention_bwd,
     joint_attention_bwd_dq_rows,
+    varlen_attention_bwd,
     hot_path,
 )

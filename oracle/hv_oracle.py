@@ -352,6 +352,42 @@ def joint_attention_bwd_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dou
     return dq
 
 
+def varlen_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                         cu_q: Sequence[int], cu_k: Sequence[int],
+                         scale: Optional[float] = None,
+                         heads: Optional[Sequence[int]] = None):
+    """Gradients of ``varlen_attention`` (packed segments), float64.
+
+    Each segment is an independent attention (its queries, its keys), so its
+    gradients are those of ``joint_attention_bwd`` on that segment alone with
+    every key valid.  ``q``, ``k``, ``v``, ``dout``: [T, H, D].  Returns
+    (dq, dk, dv), each [T, H', D]; rows outside every segment stay zero.
+    """
+    T, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    heads = list(range(H)) if heads is None else list(heads)
+    dq = np.zeros((T, len(heads), D), dtype=np.float64)
+    dk = np.zeros_like(dq)
+    dv = np.zeros_like(dq)
+    for s in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[s]), int(cu_q[s + 1]), int(cu_k[s]), int(cu_k[s + 1])
+        if q1 == q0:
+            continue
+        for hi, h in enumerate(heads):
+            qb, gb = q[q0:q1, h, :], dout[q0:q1, h, :]
+            kb, vb = k[k0:k1, h, :], v[k0:k1, h, :]
+            sc = (qb @ kb.T) * scale
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = gb @ vb.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[q0:q1, hi, :] = scale * (ds @ kb)
+            dk[k0:k1, hi, :] = scale * (ds.T @ qb)
+            dv[k0:k1, hi, :] = p.T @ gb
+    return dq, dk, dv
+
+
 def hot_path(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
              frames: int, height: int, width: int, valid: Sequence[int],
              theta: float, rows: Optional[np.ndarray] = None,

@@ -108,3 +108,49 @@ def test_dq_rows_matches_the_full_gradient():
     rows = np.array([0, 3, 10, 13])
     sub = joint_attention_bwd_dq_rows(q[:, rows], k, v, g[:, rows], N, valid)
     assert np.allclose(sub, dq[:, rows], rtol=1e-13, atol=1e-14)
+
+
+def test_varlen_bwd_finite_differences_and_isolation():
+    from oracle import varlen_attention, varlen_attention_bwd
+
+    r = np.random.default_rng(11)
+    T, H = 17, 2
+    q, k, v, g = (r.standard_normal((T, H, D)) for _ in range(4))
+    cu_q, cu_k = [0, 6, 6, 15], [0, 4, 9, 16]   # an empty query segment; row 15, 16 outside
+    dq, dk, dv = varlen_attention_bwd(q, k, v, g, cu_q, cu_k)
+
+    def lossf():
+        out, _ = varlen_attention(q, k, v, cu_q, cu_k)
+        return float(np.sum(g * out))
+
+    eps = 1e-6
+    for name, t, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(10):
+            idx = tuple(int(r.integers(0, n)) for n in t.shape)
+            old = t[idx]
+            t[idx] = old + eps
+            lp = lossf()
+            t[idx] = old - eps
+            lm = lossf()
+            t[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    # keys 4..8 belong to the empty query segment: nobody attends to them
+    assert not dk[4:9].any() and not dv[4:9].any()
+    assert not dq[15:].any() and not dk[16:].any()
+
+
+def test_varlen_bwd_matches_per_clip_joint_gradients():
+    from oracle import varlen_attention_bwd
+
+    r = np.random.default_rng(12)
+    lens = [7, 12, 5]
+    T = sum(lens)
+    q, k, v, g = (r.standard_normal((T, 3, D)) for _ in range(4))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    dq, dk, dv = varlen_attention_bwd(q, k, v, g, cu, cu)
+    for s in range(3):
+        a, b = cu[s], cu[s + 1]
+        ref = joint_attention_bwd(q[None, a:b], k[None, a:b], v[None, a:b], g[None, a:b], b - a, [0])
+        for got, want in zip((dq, dk, dv), ref):
+            assert np.allclose(got[a:b], want[0], rtol=1e-12, atol=1e-13)
