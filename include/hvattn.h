@@ -251,6 +251,30 @@ int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                            hv_bf16* dq, hv_bf16* dk, hv_bf16* dv, float* delta,
                            const hv_layout* layout, float softmax_scale, void* stream);
 
+/* hv_joint_attention_varlen_bwd: gradients of hv_joint_attention_varlen_fwd
+ * (packed segments; notes page section 9.1 for the packed form, the report
+ * summary page's Infra section for the training-side cost).  Each segment
+ * is an independent attention, so its gradients are those of
+ * hv_joint_attention_bwd on that segment with every key valid.  Rows
+ * outside every segment are not written in dq; key rows outside every
+ * segment are not written in dk, dv; key rows of a segment whose queries
+ * are empty get zero dk, dv.
+ *   q, k, v, out, dout, dq, dk, dv  T = layout->seq_len packed rows
+ *                       (layout->batch must be 1); out is the forward's
+ *                       output, dout the gradient with respect to it
+ *   lse                 device fp32 [24][T], the forward's log-sum-exp as
+ *                       hv_joint_attention_varlen_fwd writes it
+ *   cu_seqlens_q/k, n_segments, softmax_scale  as in the forward
+ *   delta               device fp32 [24][T] workspace (caller-owned)
+ * Errors: HV_ERR_INVALID_ARG (NULL, batch != 1, bad offsets, alignment,
+ * overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+int hv_joint_attention_varlen_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                                  const hv_bf16* out, const hv_bf16* dout, const float* lse,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t n_segments, hv_bf16* dq, hv_bf16* dk, hv_bf16* dv,
+                                  float* delta, const hv_layout* layout, float softmax_scale,
+                                  void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* hv_status_string(int status);
 

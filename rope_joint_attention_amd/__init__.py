@@ -18,6 +18,8 @@ not built, every call raises (there is no fallback).
                                   ...) -> (out, lse)
     hv_joint_attention_bwd(q, k, v, out, dout, lse, text_valid_len, n_video,
                            ...) -> (dq, dk, dv)
+    hv_joint_attention_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q,
+                                  cu_seqlens_k=None, ...) -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ __all__ = [
     "HV_HEADS", "HV_HEAD_DIM", "HV_MAX_BATCH", "HvError", "HvGrid",
     "hv_token_grid", "hv_rope3d_apply", "hv_qk_norm_rope3d_apply", "hv_joint_attention_fwd",
     "hv_attention_fwd_lse", "hv_attention_merge", "hv_joint_attention_varlen_fwd",
-    "hv_joint_attention_bwd",
+    "hv_joint_attention_bwd", "hv_joint_attention_varlen_bwd",
     "hv_status_string", "library_path", "load_library",
 ]
 
@@ -133,6 +135,10 @@ def load_library():
         ctypes.POINTER(ctypes.c_int32), ctypes.c_int64] + [ctypes.c_void_p] * 4 + [
         ctypes.POINTER(_Layout), ctypes.c_float, ctypes.c_void_p]
     lib.hv_joint_attention_bwd.restype = ctypes.c_int
+    lib.hv_joint_attention_varlen_bwd.argtypes = [ctypes.c_void_p] * 6 + [
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32] + [
+        ctypes.c_void_p] * 4 + [ctypes.POINTER(_Layout), ctypes.c_float, ctypes.c_void_p]
+    lib.hv_joint_attention_varlen_bwd.restype = ctypes.c_int
     lib.hv_status_string.argtypes = [ctypes.c_int]
     lib.hv_status_string.restype = ctypes.c_char_p
     lib.hv_version.argtypes = []
@@ -407,4 +413,49 @@ def hv_joint_attention_bwd(q, k, v, out, dout, lse, text_valid_len: Optional[Seq
                                                _stream_of(q))
     if st != HV_OK:
         raise HvError(st, "hv_joint_attention_bwd")
+    return tuple(grads)
+
+
+def hv_joint_attention_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q: Sequence[int],
+                                  cu_seqlens_k: Optional[Sequence[int]] = None, dq=None, dk=None,
+                                  dv=None, delta=None, softmax_scale: Optional[float] = None):
+    """Gradients of hv_joint_attention_varlen_fwd (see hvattn.h).  q, k, v, out,
+    dout: [T, 24, 128] packed rows sharing shape and strides; lse: the forward's
+    float32 [24, T].  Returns (dq, dk, dv)."""
+    import torch
+
+    def as4(t, name):
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [T, {HV_HEADS}, {HV_HEAD_DIM}]")
+        return t.unsqueeze(0)
+
+    lay = _layout_of(as4(q, "q"), "q")
+    for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        if not _same_layout(lay, _layout_of(as4(t, name), name)):
+            raise ValueError(f"q and {name} must share shape and strides")
+    shape = (HV_HEADS, q.shape[0])
+    _lse_buffer(lse, shape, q.device, "lse")
+    delta = _lse_buffer(delta, shape, q.device, "delta")
+    grads = []
+    for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if g is None:
+            g = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+        elif not _same_layout(lay, _layout_of(as4(g, name), name)):
+            raise ValueError(f"{name} must share shape and strides with q")
+        grads.append(g)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = cq if cu_seqlens_k is None else [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or len(cq) < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need n_segments + 1 entries each")
+    aq = (ctypes.c_int32 * len(cq))(*cq)
+    ak = (ctypes.c_int32 * len(ck))(*ck)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = load_library().hv_joint_attention_varlen_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                      out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                                      aq, ak, len(cq) - 1, grads[0].data_ptr(),
+                                                      grads[1].data_ptr(), grads[2].data_ptr(),
+                                                      delta.data_ptr(), ctypes.byref(lay), scale,
+                                                      _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_joint_attention_varlen_bwd")
     return tuple(grads)

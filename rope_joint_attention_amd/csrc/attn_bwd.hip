@@ -226,15 +226,19 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   const int hh = lane >> 5;
 
   const int logical = logical_block(p.n_kv_blocks);
-  const int kb = logical % p.n_kblocks;
-  const int bh = logical / p.n_kblocks;
-  const int head = bh % HV_HEADS;
-  const int b = bh / HV_HEADS;
-  const int L = p.seq_len;
-  const int Lk = p.lk[b];
+  int si = 0;  // segment of this block (uniform scan over at most 64 entries)
+  for (int i = 1; i < p.n_seg; ++i)
+    if (logical >= p.seg[i].k_blk) si = i;
+  const BwdSegment& sg = p.seg[si];
+  const int rel = logical - sg.k_blk;
+  const int head = rel / sg.nkb;
+  const int kb = rel - head * sg.nkb;
+  const int L = sg.q_len;    // query rows
+  const int Lk = sg.k_len;   // valid keys
   const int64_t sl = p.stride_l;
-  const int64_t hbase = (int64_t)b * p.stride_b + (int64_t)head * D;
-  const int64_t vbase = ((int64_t)b * HV_HEADS + head) * L;  // lse / delta row 0
+  const int64_t qbase = sg.q_off + (int64_t)head * D;
+  const int64_t kbase = sg.k_off + (int64_t)head * D;
+  const int64_t vbase = sg.v_off + (int64_t)head * p.v_hstride;  // lse / delta row 0
 
   // K and V of this lane's key as the B operands (n = key, k = channels
   // 16kc + 8hh .. +7); keys past the valid ones read the last valid row and
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   const bool key_ok = key < Lk;
   bf16x8 kf[8], vf[8];
   {
-    const int64_t r = hbase + (int64_t)min(key, Lk - 1) * sl + hh * 8;
+    const int64_t r = kbase + (int64_t)min(key, Lk - 1) * sl + hh * 8;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       kf[kc] = *reinterpret_cast<const bf16x8*>(p.k + r + kc * 16);
@@ -262,12 +266,12 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float c2 = p.scale_log2;
   // a block of padded keys only has zero gradients: skip the query loop
-  const int nq = kb * KV_KEYS >= Lk ? 0 : (L + TR - 1) / TR;
+  const int nq = kb * KV_KEYS >= Lk || L == 0 ? 0 : (L + TR - 1) / TR;
 
   // 16 instructions per 64-row tile and tensor: wave w issues 4w .. 4w+3
   auto load = [&](auto st, int t) {
-    stage_tile(p.q + hbase, sl, t * TR, L - 1, qbuf(st), 4 * wave, 4, lane);
-    stage_tile(p.dout + hbase, sl, t * TR, L - 1, gbuf(st), 4 * wave, 4, lane);
+    stage_tile(p.q + qbase, sl, t * TR, L - 1, qbuf(st), 4 * wave, 4, lane);
+    stage_tile(p.dout + qbase, sl, t * TR, L - 1, gbuf(st), 4 * wave, 4, lane);
     if (wave == 0) stage_vec(p.lse + vbase, t * TR, L - 1, lbuf(st), lane);
     if (wave == 1) stage_vec(p.delta + vbase, t * TR, L - 1, dbuf(st), lane);
   };
@@ -359,10 +363,10 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
   // lane owns key `key`, channels 32dt + 8j + 4hh .. +3 (register 4j .. 4j+3)
-  if (key < L) {
+  if (key < sg.k_rows) {
     const float sc = p.scale;
-    uint16_t* kp = p.dk + hbase + (int64_t)key * sl;
-    uint16_t* vp = p.dv + hbase + (int64_t)key * sl;
+    uint16_t* kp = p.dk + kbase + (int64_t)key * sl;
+    uint16_t* vp = p.dv + kbase + (int64_t)key * sl;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -395,22 +399,26 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
   const int hh = lane >> 5;
 
   const int logical = logical_block(p.n_q_blocks);
-  const int qb = logical % p.n_qblocks;
-  const int bh = logical / p.n_qblocks;
-  const int head = bh % HV_HEADS;
-  const int b = bh / HV_HEADS;
-  const int L = p.seq_len;
-  const int Lk = p.lk[b];
+  int si = 0;
+  for (int i = 1; i < p.n_seg; ++i)
+    if (logical >= p.seg[i].q_blk) si = i;
+  const BwdSegment& sg = p.seg[si];
+  const int rel = logical - sg.q_blk;
+  const int head = rel / sg.nqb;
+  const int qb = rel - head * sg.nqb;
+  const int L = sg.q_len;
+  const int Lk = sg.k_len;
   const int64_t sl = p.stride_l;
-  const int64_t hbase = (int64_t)b * p.stride_b + (int64_t)head * D;
-  const int64_t vbase = ((int64_t)b * HV_HEADS + head) * L;
+  const int64_t qbase = sg.q_off + (int64_t)head * D;
+  const int64_t kbase = sg.k_off + (int64_t)head * D;
+  const int64_t vbase = sg.v_off + (int64_t)head * p.v_hstride;
 
   // Q and dO of this lane's query as B operands (n = query, k = channels)
   const int q0 = qb * Q_ROWS + wave * 32;
   const int qrow = min(q0 + l32, L - 1);  // rows past the end are computed, never stored
   bf16x8 qf[8], gf[8];
   {
-    const int64_t r = hbase + (int64_t)qrow * sl + hh * 8;
+    const int64_t r = qbase + (int64_t)qrow * sl + hh * 8;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       qf[kc] = *reinterpret_cast<const bf16x8*>(p.q + r + kc * 16);
@@ -435,8 +443,8 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
   // 16 instructions per tile and tensor, split evenly over the waves
   constexpr int per_wave = 16 / Q_WAVES;
   auto load = [&](auto st, int t) {
-    stage_tile(p.k + hbase, sl, t * TR, Lk - 1, kbuf(st), per_wave * wave, per_wave, lane);
-    stage_tile(p.v + hbase, sl, t * TR, Lk - 1, vbuf(st), per_wave * wave, per_wave, lane);
+    stage_tile(p.k + kbase, sl, t * TR, Lk - 1, kbuf(st), per_wave * wave, per_wave, lane);
+    stage_tile(p.v + kbase, sl, t * TR, Lk - 1, vbuf(st), per_wave * wave, per_wave, lane);
   };
 
   auto tile = [&](auto st, int t) {
@@ -491,7 +499,7 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
   const int orow = q0 + l32;
   if (orow < L) {
     const float sc = p.scale;
-    uint16_t* op = p.dq + hbase + (int64_t)orow * sl;
+    uint16_t* op = p.dq + qbase + (int64_t)orow * sl;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -507,17 +515,27 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
 }  // namespace
 
 hipError_t launch_attn_bwd(BwdParams& p, hipStream_t stream) {
-  p.n_qblocks = (p.seq_len + Q_ROWS - 1) / Q_ROWS;
-  p.n_kblocks = (p.seq_len + KV_KEYS - 1) / KV_KEYS;
-  p.n_q_blocks = p.batch * HV_HEADS * p.n_qblocks;
-  p.n_kv_blocks = p.batch * HV_HEADS * p.n_kblocks;
+  int qblocks = 0, kblocks = 0;
+  for (int i = 0; i < p.n_seg; ++i) {
+    BwdSegment& sg = p.seg[i];
+    sg.nqb = (sg.q_len + Q_ROWS - 1) / Q_ROWS;
+    sg.nkb = (sg.k_rows + KV_KEYS - 1) / KV_KEYS;  // also zero-fills keys nobody attends to
+    sg.q_blk = qblocks;
+    sg.k_blk = kblocks;
+    qblocks += HV_HEADS * sg.nqb;
+    kblocks += HV_HEADS * sg.nkb;
+  }
+  p.n_q_blocks = qblocks;
+  p.n_kv_blocks = kblocks;
+  if (qblocks == 0 && kblocks == 0) return hipSuccess;
   const int64_t threads = (int64_t)p.batch * p.seq_len * 16;
-  hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, p);
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)p.n_kv_blocks), dim3(KV_WAVES * 64), 0,
-                     stream, p);
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)p.n_q_blocks), dim3(Q_WAVES * 64), 0, stream,
-                     p);
+  if (threads > 0 && qblocks > 0)  // D is only read when some segment has queries
+    hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, p);
+  if (kblocks > 0)
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)kblocks), dim3(KV_WAVES * 64), 0, stream, p);
+  if (qblocks > 0)
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)qblocks), dim3(Q_WAVES * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -114,30 +114,54 @@ struct MergeParams {
 hipError_t launch_attn_merge(const MergeParams& p, hipStream_t stream);
 
 // ---- attention backward -----------------------------------------------------
+// Segments as in the forward: segment s has q_len query rows from element
+// q_off (q, o, dout, dq) and k_rows key rows from element k_off (k, v, dk,
+// dv), of which the first k_len are valid keys; the rest get zero dk, dv.
+// Its lse / delta values sit at v_off + head * v_hstride + row.
+struct BwdSegment {
+  int64_t q_off;
+  int64_t k_off;
+  int64_t v_off;
+  int32_t q_len;
+  int32_t k_rows;
+  int32_t k_len;     // >= 1 when q_len > 0
+  int32_t q_blk;     // first block of the dq kernel
+  int32_t k_blk;     // first block of the dkdv kernel
+  int32_t nqb;       // dq blocks per head
+  int32_t nkb;       // dkdv blocks per head
+  int32_t pad_;
+};
+
 struct BwdParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   const uint16_t* o;
   const uint16_t* dout;
-  const float* lse;    // [batch][24][seq_len], natural log
-  float* delta;        // [batch][24][seq_len], written by the first kernel
+  const float* lse;    // natural log, per (head, row) as the segments place it
+  float* delta;        // same placement, written by the first kernel
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  int64_t stride_b;    // elements, shared by all bf16 tensors
+  int64_t stride_b;    // elements, shared by all bf16 tensors (delta pass)
   int64_t stride_l;
-  int32_t batch;
-  int32_t seq_len;
+  int64_t v_hstride;   // lse / delta elements between heads
+  int32_t batch;       // the delta pass covers batch x seq_len rows,
+  int32_t seq_len;     // delta[(b * 24 + h) * seq_len + n]
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e)
-  int32_t n_qblocks;   // query blocks per (batch, head) of the dq kernel
-  int32_t n_kblocks;   // key blocks per (batch, head) of the dkdv kernel
+  int32_t n_seg;
   int32_t n_q_blocks;  // dq workgroups
   int32_t n_kv_blocks; // dkdv workgroups
-  int32_t lk[HV_MAX_BATCH];  // valid keys per batch entry
+  int32_t pad_;
+  BwdSegment seg[kMaxSegments];
 };
 
 hipError_t launch_attn_bwd(BwdParams& p, hipStream_t stream);
+
+// Kernel arguments are passed by value; keep them within 4 KB.
+static_assert(sizeof(AttnParams) <= 4096, "attention kernel arguments exceed 4 KB");
+static_assert(sizeof(BwdParams) <= 4096, "backward kernel arguments exceed 4 KB");
+static_assert(sizeof(MergeParams) <= 4096, "merge kernel arguments exceed 4 KB");
 
 }  // namespace hv

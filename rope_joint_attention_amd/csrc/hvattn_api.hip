@@ -76,6 +76,64 @@ float scale_log2(float softmax_scale) {
   return (float)((double)scale * 1.4426950408889634);  // log2(e)
 }
 
+// Pointers, alignment and overlap of the backward's arguments (shared by the
+// padded and the packed forms).  lse and delta hold batch * 24 * seq_len floats.
+int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, const hv_bf16* out,
+                      const hv_bf16* dout, const float* lse, hv_bf16* dq, hv_bf16* dk, hv_bf16* dv,
+                      float* delta, const hv_layout* layout) {
+  int64_t extent = 0;
+  int st = check_layout(layout, &extent);
+  if (st != HV_OK) return st;
+  const hv_bf16* ins[5] = {q, k, v, out, dout};
+  hv_bf16* outs[3] = {dq, dk, dv};
+  for (const hv_bf16* t : ins)
+    if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
+  for (const hv_bf16* t : outs)
+    if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
+  if (!lse || !delta || ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)delta & 3u) != 0)
+    return HV_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i) {
+    for (const hv_bf16* t : ins)
+      if (overlap(outs[i], t, layout, extent)) return HV_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j], layout, extent)) return HV_ERR_INVALID_ARG;
+  }
+  const uintptr_t vb = (uintptr_t)layout->batch * HV_HEADS * layout->seq_len * sizeof(float);
+  const uintptr_t tb = (uintptr_t)extent * sizeof(hv_bf16);
+  if (ranges_meet(delta, vb, lse, vb)) return HV_ERR_INVALID_ARG;
+  for (const hv_bf16* t : ins)
+    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
+  for (const hv_bf16* t : outs)
+    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
+  return HV_OK;
+}
+
+// Fill the parts of BwdParams shared by both forms and launch.
+int launch_bwd(hv::BwdParams& p, const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+               const hv_bf16* out, const hv_bf16* dout, const float* lse, hv_bf16* dq,
+               hv_bf16* dk, hv_bf16* dv, float* delta, const hv_layout* layout,
+               float softmax_scale, void* stream) {
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.stride_b = layout->stride_b;
+  p.stride_l = layout->stride_l;
+  p.v_hstride = layout->seq_len;
+  p.batch = layout->batch;
+  p.seq_len = layout->seq_len;
+  p.scale_log2 = scale_log2(softmax_scale);
+  p.scale = (float)((double)p.scale_log2 / 1.4426950408889634);
+  const hipError_t e = hv::launch_attn_bwd(p, (hipStream_t)stream);
+  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+}
+
 int check_grid(const hv_grid* g) {
   if (!g) return HV_ERR_INVALID_ARG;
   if (g->gt <= 0 || g->gh <= 0 || g->gw <= 0) return HV_ERR_INVALID_ARG;
@@ -360,60 +418,59 @@ int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                            const int32_t* text_valid_len, int64_t n_video, hv_bf16* dq,
                            hv_bf16* dk, hv_bf16* dv, float* delta, const hv_layout* layout,
                            float softmax_scale, void* stream) {
-  int64_t extent = 0;
-  int st = check_layout(layout, &extent);
+  int st = check_bwd_buffers(q, k, v, out, dout, lse, dq, dk, dv, delta, layout);
   if (st != HV_OK) return st;
   if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
-  const hv_bf16* ins[5] = {q, k, v, out, dout};
-  hv_bf16* outs[3] = {dq, dk, dv};
-  for (const hv_bf16* t : ins)
-    if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
-  for (const hv_bf16* t : outs)
-    if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
-  if (!lse || !delta || ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)delta & 3u) != 0)
-    return HV_ERR_INVALID_ARG;
-  for (int i = 0; i < 3; ++i) {
-    for (const hv_bf16* t : ins)
-      if (overlap(outs[i], t, layout, extent)) return HV_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 3; ++j)
-      if (overlap(outs[i], outs[j], layout, extent)) return HV_ERR_INVALID_ARG;
-  }
-  const uintptr_t vb = (uintptr_t)layout->batch * HV_HEADS * layout->seq_len * sizeof(float);
-  const uintptr_t tb = (uintptr_t)extent * sizeof(hv_bf16);
-  if (ranges_meet(delta, vb, lse, vb)) return HV_ERR_INVALID_ARG;
-  for (const hv_bf16* t : ins)
-    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
-  for (const hv_bf16* t : outs)
-    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
   if (layout->batch == 0 || layout->seq_len == 0) return HV_OK;
 
   hv::BwdParams p;
   memset(&p, 0, sizeof(p));
   const int64_t text_cap = layout->seq_len - n_video;
+  const int L = layout->seq_len;
   for (int b = 0; b < layout->batch; ++b) {
     const int64_t valid = text_valid_len ? text_valid_len[b] : text_cap;
     if (valid < 0 || valid > text_cap) return HV_ERR_INVALID_ARG;
     if (n_video + valid < 1) return HV_ERR_INVALID_ARG;
-    p.lk[b] = (int32_t)(n_video + valid);
+    hv::BwdSegment& sg = p.seg[b];
+    sg.q_off = sg.k_off = (int64_t)b * layout->stride_b;
+    sg.v_off = (int64_t)b * HV_HEADS * L;
+    sg.q_len = sg.k_rows = L;
+    sg.k_len = (int32_t)(n_video + valid);
   }
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.o = out;
-  p.dout = dout;
-  p.lse = lse;
-  p.delta = delta;
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  p.stride_b = layout->stride_b;
-  p.stride_l = layout->stride_l;
-  p.batch = layout->batch;
-  p.seq_len = layout->seq_len;
-  p.scale_log2 = scale_log2(softmax_scale);
-  p.scale = (float)((double)p.scale_log2 / 1.4426950408889634);
-  const hipError_t e = hv::launch_attn_bwd(p, (hipStream_t)stream);
-  return e == hipSuccess ? HV_OK : HV_ERR_HIP;
+  p.n_seg = layout->batch;
+  return launch_bwd(p, q, k, v, out, dout, lse, dq, dk, dv, delta, layout, softmax_scale, stream);
+}
+
+int hv_joint_attention_varlen_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                                  const hv_bf16* out, const hv_bf16* dout, const float* lse,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                  int32_t n_segments, hv_bf16* dq, hv_bf16* dk, hv_bf16* dv,
+                                  float* delta, const hv_layout* layout, float softmax_scale,
+                                  void* stream) {
+  int st = check_bwd_buffers(q, k, v, out, dout, lse, dq, dk, dv, delta, layout);
+  if (st != HV_OK) return st;
+  if (layout->batch != 1) return HV_ERR_INVALID_ARG;
+  if (n_segments < 1 || n_segments > HV_MAX_SEGMENTS) return HV_ERR_INVALID_ARG;
+  if (!cu_seqlens_q || !cu_seqlens_k) return HV_ERR_INVALID_ARG;
+  if (cu_seqlens_q[0] < 0 || cu_seqlens_k[0] < 0) return HV_ERR_INVALID_ARG;
+  const int T = layout->seq_len;
+  hv::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  for (int s = 0; s < n_segments; ++s) {
+    const int32_t q0 = cu_seqlens_q[s], q1 = cu_seqlens_q[s + 1];
+    const int32_t k0 = cu_seqlens_k[s], k1 = cu_seqlens_k[s + 1];
+    if (q1 < q0 || k1 < k0 || q1 > T || k1 > T) return HV_ERR_INVALID_ARG;
+    if (q1 > q0 && k1 == k0) return HV_ERR_INVALID_ARG;  // queries with no key
+    hv::BwdSegment& sg = p.seg[s];
+    sg.q_off = (int64_t)q0 * layout->stride_l;
+    sg.k_off = (int64_t)k0 * layout->stride_l;
+    sg.v_off = q0;
+    sg.q_len = q1 - q0;
+    sg.k_rows = sg.k_len = k1 - k0;
+  }
+  if (T == 0) return HV_OK;
+  p.n_seg = n_segments;
+  return launch_bwd(p, q, k, v, out, dout, lse, dq, dk, dv, delta, layout, softmax_scale, stream);
 }
 
 int hv_attention_merge(const hv_bf16* const* outs, const float* const* lses, int32_t n_parts,

@@ -383,3 +383,34 @@ def test_backward_validation(kwargs, expect):
 
 def test_backward_empty_call():
     assert bwd(lay=layout(batch=0), valid=None, n_video=0) == hv.HV_OK
+
+
+def varlen_bwd(cq=(0, 100, 300), ck=None, n=None, lay=None, **kw):
+    lib = hv.load_library()
+    ck = cq if ck is None else ck
+    n = len(cq) - 1 if n is None else n
+    aq = (ctypes.c_int32 * len(cq))(*cq)
+    ak = (ctypes.c_int32 * len(ck))(*ck)
+    lay = layout() if lay is None else lay
+    a = dict(q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP, o=FAKE + 3 * SEP, g=FAKE + 4 * SEP, lse=LSE,
+             dq=FAKE + 10 * SEP, dk=FAKE + 11 * SEP, dv=FAKE + 12 * SEP, delta=FAKE + 13 * SEP)
+    a.update(kw)
+    return lib.hv_joint_attention_varlen_bwd(a["q"], a["k"], a["v"], a["o"], a["g"], a["lse"], aq, ak, n,
+                                             a["dq"], a["dk"], a["dv"], a["delta"], ctypes.byref(lay),
+                                             0.0, None)
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(dk=0), E), (dict(lse=0), E), (dict(delta=LSE + 128), E),
+    (dict(n=0), E), (dict(cq=(0, 100, 301)), E), (dict(cq=(0, 120, 100)), E),
+    (dict(cq=(0, 100, 300), ck=(0, 100, 100)), E),
+    (dict(lay=layout(batch=2, sb=300 * 3072)), E),
+    (dict(dv=FAKE + 2 * SEP + 64), E),
+    (dict(lay=layout(heads=12)), U),
+])
+def test_varlen_bwd_validation(kwargs, expect):
+    assert varlen_bwd(**kwargs) == expect
+
+
+def test_varlen_bwd_empty_segments_launch_nothing():
+    assert varlen_bwd(cq=(0, 0, 0), ck=(0, 0, 0)) == hv.HV_OK

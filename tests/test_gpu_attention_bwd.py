@@ -164,3 +164,69 @@ def test_bwd_maximum_batch():
                               valid, heads=[0, 7, 23])
     for i, (name, got) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
         grad_close(widen(got[:, :, [0, 7, 23]]), ref[i], name)
+
+
+def run_varlen_bwd(bits, dout_bits, cq, ck):
+    import torch
+    import rope_joint_attention_amd as hv
+
+    q, k, v = (bits_to_torch(bits[n])[0] for n in "qkv")
+    out, lse = hv.hv_joint_attention_varlen_fwd(q, k, v, cq, ck, want_lse=True)
+    g = bits_to_torch(dout_bits)[0]
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    hv.hv_joint_attention_varlen_bwd(q, k, v, out, g, lse, cq, ck, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return torch_to_bits(dq), torch_to_bits(dk), torch_to_bits(dv)
+
+
+def test_varlen_bwd_packed_clips():
+    from oracle import varlen_attention_bwd
+
+    lens = [16 + 13, 30, 256 + 200, 24 + 77]   # clips [video | valid text] of the forward test
+    cu = [0] + list(np.cumsum(lens))
+    T = cu[-1]
+    bits, dout = draw(1, T, seed=2121)
+    log(f"varlen bwd clips T={T} cu={cu}")
+    dq, dk, dv = run_varlen_bwd(bits, dout, cu, cu)
+    ref = varlen_attention_bwd(widen(bits["q"][0]), widen(bits["k"][0]), widen(bits["v"][0]),
+                               widen(dout[0]), cu, cu)
+    for name, got, r in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        log(f"  {name} {grad_close(widen(got), r, name)}")
+
+
+def test_varlen_bwd_cross_segments_and_untouched_rows():
+    from oracle import varlen_attention_bwd
+
+    T = 700
+    bits, dout = draw(1, T, seed=3131)
+    cq = [0, 100, 100, 400, 650]     # an empty query segment; rows 650.. belong to none
+    ck = [0, 50, 60, 600, 690]       # keys 50..59 belong to the empty segment; 690.. to none
+    dq, dk, dv = run_varlen_bwd(bits, dout, cq, ck)
+    ref = varlen_attention_bwd(widen(bits["q"][0]), widen(bits["k"][0]), widen(bits["v"][0]),
+                               widen(dout[0]), cq, ck)
+    assert np.isnan(widen(dq[650:])).all()
+    assert np.isnan(widen(dk[690:])).all() and np.isnan(widen(dv[690:])).all()
+    assert not widen(dk[50:60]).any() and not widen(dv[50:60]).any()   # zero-filled
+    grad_close(widen(dq[:650]), ref[0][:650], "dq")
+    grad_close(widen(dk[:690]), ref[1][:690], "dk")
+    grad_close(widen(dv[:690]), ref[2][:690], "dv")
+
+
+def test_varlen_bwd_padded_batch_reading():
+    # a padded batch of two entries flattened into [valid | padded tail]
+    # segments, each tail attending to itself
+    from oracle import varlen_attention_bwd
+
+    B, N, cap, valid = 2, 600, 100, (37, 100)
+    L = N + cap
+    bits, dout = draw(B, L, seed=4141)
+    flat = {n: bits[n].reshape(1, B * L, 24, 128) for n in "qkv"}
+    cu = [0]
+    for b in range(B):
+        cu += [b * L + N + valid[b], (b + 1) * L]
+    log(f"varlen bwd padded batch cu={cu}")
+    dq, dk, dv = run_varlen_bwd(flat, dout.reshape(1, B * L, 24, 128), cu, cu)
+    ref = varlen_attention_bwd(widen(flat["q"][0]), widen(flat["k"][0]), widen(flat["v"][0]),
+                               widen(dout.reshape(B * L, 24, 128)), cu, cu)
+    for i, (name, got) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
+        log(f"  {name} {grad_close(widen(got), ref[i], name)}")
