@@ -28,8 +28,9 @@
  *     holds the n_video video tokens first, then the text tokens.
  *   - Device pointers must be 16-byte aligned; strides must be multiples of
  *     8 elements, stride_l >= heads*head_dim, stride_b >= seq_len*stride_l.
- *   - heads must be 24 and head_dim 128, batch <= HV_MAX_BATCH and
- *     seq_len <= HV_MAX_SEQ (HV_ERR_UNSUPPORTED otherwise); negative sizes
+ *   - heads must be 24 and head_dim 128, batch <= HV_MAX_BATCH,
+ *     seq_len <= HV_MAX_SEQ and stride_l <= HV_MAX_TOKEN_STRIDE
+ *     (HV_ERR_UNSUPPORTED otherwise); negative sizes
  *     are HV_ERR_INVALID_ARG.  A call with batch == 0 or seq_len == 0 has
  *     nothing to do and returns HV_OK without launching (so does RoPE with
  *     n_video == 0).
@@ -56,6 +57,7 @@ extern "C" {
 #define HV_HEAD_DIM 128
 #define HV_MAX_BATCH 64
 #define HV_MAX_SEQ (1 << 24)
+#define HV_MAX_TOKEN_STRIDE (1 << 24) /* elements between consecutive tokens */
 #define HV_MAX_SEGMENTS 64    /* packed segments per varlen call */
 #define HV_MAX_MERGE_PARTS 16 /* partial results per merge call */
 

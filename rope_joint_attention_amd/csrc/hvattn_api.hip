@@ -21,6 +21,8 @@ int check_layout(const hv_layout* lay, int64_t* extent) {
   if (lay->heads != HV_HEADS || lay->head_dim != HV_HEAD_DIM) return HV_ERR_UNSUPPORTED;
   if (lay->batch > HV_MAX_BATCH || lay->seq_len > HV_MAX_SEQ) return HV_ERR_UNSUPPORTED;
   if (lay->stride_l < kRowElems || (lay->stride_l & 7) != 0) return HV_ERR_INVALID_ARG;
+  // per-lane offsets inside a 64-row tile are 32-bit: 64 * 2 * stride_l < 2^32
+  if (lay->stride_l > HV_MAX_TOKEN_STRIDE) return HV_ERR_UNSUPPORTED;
   if ((lay->stride_b & 7) != 0) return HV_ERR_INVALID_ARG;
   if (lay->batch > 1 && lay->stride_b < (int64_t)lay->seq_len * lay->stride_l)
     return HV_ERR_INVALID_ARG;

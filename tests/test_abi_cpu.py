@@ -134,6 +134,7 @@ E, U = hv.HV_ERR_INVALID_ARG, hv.HV_ERR_UNSUPPORTED
     (dict(lay=layout(seq=(1 << 24) + 1)), U),
     (dict(lay=layout(batch=-1)), E), (dict(lay=layout(seq=-5)), E),
     (dict(lay=layout(sl=3000)), E), (dict(lay=layout(sl=3076)), E),
+    (dict(lay=layout(sl=(1 << 24) + 8)), U),             # token stride beyond the 32-bit tile offsets
     (dict(lay=layout(batch=2, sb=3072 * 10)), E),         # batch stride too small
     (dict(lay=layout(seq=39)), E),                        # fewer rows than video tokens
 ])
