@@ -7,9 +7,16 @@
 // change the result), so the kernel is a tiled exact softmax: scores are
 // never written to memory.
 //
+// The same kernel serves the padded batch, packed segments (variable-length
+// clips, section 9.1) and one query block against one K/V block of a
+// sequence-parallel ring (section 9.2): its work list is a table of segments
+// (query rows, key rows, output rows), and it can also write the natural-log
+// log-sum-exp of every row, which lets results over disjoint K/V blocks be
+// merged exactly.
+//
 // Work decomposition
-//   * one workgroup = (batch, head, 256 query rows); 8 waves of 32 rows, two
-//     waves per SIMD;
+//   * one workgroup = (segment, head, 256 query rows); 8 waves of 32 rows,
+//     two waves per SIMD;
 //   * K and V tiles of 64 keys reach LDS by direct global->LDS loads
 //     (global_load_lds_dwordx4: no registers, fully coalesced 1 KB per wave
 //     instruction) into four LDS stages each for K and V; K tile t+4 and
@@ -34,11 +41,12 @@
 //   softmax VALU work of tile t, the PV MFMAs of tile t under the row maximum
 //   of tile t+1.
 // LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled within a row (K:
-// slot c ^ (r % 16), V: slot c ^ 4(r % 4)) so that both the K operand reads and
-// the transposing V reads run without bank conflicts.  The padded-key mask is a loop bound plus a predicate on
-// the last tile.  Rows past the valid keys are never read: their loads are
-// clamped to the last valid row, whose scores are masked to -inf (K) or whose
-// weights are exactly zero (V), so padding contents cannot reach the output.
+// slot c ^ (r % 16), V: slot c ^ 4(r % 4)) so that both the K operand reads
+// and the transposing V reads run without bank conflicts.  The padded-key
+// mask is a loop bound plus a predicate on the last tile.  Rows past the
+// valid keys are never read: their loads are clamped to the last valid row,
+// whose scores are masked to -inf (K) or whose weights are exactly zero (V),
+// so padding contents cannot reach the output.
 #include <type_traits>
 
 #include "hv_internal.h"
