@@ -126,6 +126,8 @@ def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int)
     varlen_pack: the batch of two 720x1280x33 clips with 37 and 256 valid text
       tokens packed as [valid | padded tail] segments of one sequence (the
       padded tails attend to themselves), one hv_joint_attention_varlen_fwd.
+    workloads: attention and RoPE of each of the five workloads (device-side
+      random inputs of the workload's shape, timing only).
     backward: hv_joint_attention_bwd at this size.  `tflops` counts the usual
       five matrix products of an attention backward (2.5x the forward's
       FLOPs); the kernels execute seven (S and dP are formed twice, once for
@@ -185,6 +187,30 @@ def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int)
         out["varlen_pack"] = {"workload": wb.name, "segments": len(cu) - 1, "rows": T,
                               "ms": round(ms_v, 4), "tflops": round(flv / (ms_v / 1e3) / 1e12, 2)}
         del op
+
+    # every workload's attention and RoPE time (device-side random bf16 inputs
+    # of the workload's shape; timing only)
+    wlt = {}
+    for name, w in hvinputs.WORKLOADS.items():
+        gw = hv.hv_token_grid(w.frames, w.height, w.width)
+        Lw = gw.n_video + w.text_capacity
+        gen = torch.Generator(device=q.device).manual_seed(w.seed)
+        qw, kw, vw = (torch.randn((w.batch, Lw, HEADS, HEAD_DIM), device=q.device, generator=gen)
+                      .to(torch.bfloat16) for _ in range(3))
+        ow = torch.empty_like(qw)
+        ms_a = timed(torch, stream, lambda: hv.hv_joint_attention_fwd(
+            qw, kw, vw, list(w.valid), gw.n_video, out=ow), reps)
+        ms_r = timed(torch, stream, lambda: hv.hv_rope3d_apply(qw, kw, gw, w.theta), reps)
+        lkw = [gw.n_video + x for x in w.valid]
+        flw = 4.0 * HEADS * HEAD_DIM * Lw * sum(lkw)
+        rbytes = 4.0 * w.batch * gw.n_video * HEADS * HEAD_DIM * 2
+        wlt[name] = {"seq_len": Lw, "attn_ms": round(ms_a, 4),
+                     "attn_tflops": round(flw / (ms_a / 1e3) / 1e12, 2),
+                     "pct_mfma_peak": round(100.0 * flw / (ms_a / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "rope_ms": round(ms_r, 4),
+                     "rope_GBps": round(rbytes / (ms_r / 1e3) / 1e9, 1)}
+        del qw, kw, vw, ow
+    out["workloads"] = wlt
 
     # backward of the headline attention: forward with log-sum-exp once, then
     # the gradients for an upstream gradient (v's values stand in for dO)
