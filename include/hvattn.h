@@ -40,7 +40,8 @@
  *     and the call returns without synchronising.  Faults inside a kernel
  *     surface at the caller's next synchronisation.
  *   - The library allocates no memory and keeps no mutable global state;
- *     calls are thread-safe.  Calls that write overlapping memory on
+ *     calls are thread-safe.  Scratch memory comes in as workspace
+ *     arguments (the forward calls' packed V, the backward's D).  Calls that write overlapping memory on
  *     different streams race, as with any kernel.
  *   - No C++ exception crosses this interface.
  */
@@ -140,6 +141,26 @@ int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
                             const hv_bf16* gamma_q_text, const hv_bf16* gamma_k_text,
                             float eps, void* stream);
 
+/* Workspace of the attention forward calls (hv_joint_attention_fwd,
+ * hv_attention_fwd_lse, hv_joint_attention_varlen_fwd).  With a workspace the
+ * call first rewrites V, tile by tile, channel-major into it (one pass over V,
+ * 2 x |V| bytes of HBM traffic) and the attention then reads every P V operand
+ * with a plain 16-byte LDS read; with workspace == NULL it gathers them from V
+ * in place with the transposing LDS read, about 6 % slower at the largest
+ * sizes.  Both give bitwise identical results.  A call needs, over its
+ * segments with query rows (a batch entry of the padded forms, a packed
+ * clip), sum ceil(keys / 64) * 64 * 24 * 128 * 2 bytes;
+ * hv_attention_workspace_bytes(n_keys, n_segments) returns an upper bound
+ * for n_keys keys in all over n_segments segments:
+ *   hv_joint_attention_fwd         n_keys = batch * seq_len, n_segments = batch
+ *   hv_attention_fwd_lse           n_keys = batch * kv seq_len, n_segments = batch
+ *   hv_joint_attention_varlen_fwd  n_keys = T, n_segments as passed
+ * The workspace is device memory, 16-byte aligned, disjoint from every other
+ * argument, overwritten by the call and free again when the call's work on
+ * its stream has finished.  Calls in flight together need separate
+ * workspaces.  Returns 0 for negative arguments. */
+int64_t hv_attention_workspace_bytes(int64_t n_keys, int32_t n_segments);
+
 /* hv_joint_attention_fwd: out = softmax(scale * Q K^T) V per (batch, head)
  * over the joint [video; text] sequence (notes page section 5.2).
  * Keys at positions >= n_video + text_valid_len[b] are padding and take no
@@ -152,13 +173,16 @@ int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
  *   out             device pointer, same layout; must not overlap q, k, v
  *   n_video         video tokens at the head of the sequence, 0..seq_len
  *   softmax_scale   > 0 to override; <= 0 or NaN selects 1/sqrt(128)
+ *   workspace, workspace_bytes  packed-V workspace (see above) or NULL, 0;
+ *                   too small a workspace is HV_ERR_INVALID_ARG
  * n_video + text_valid_len[b] must be >= 1 for every b.  batch == 0 or
  * seq_len == 0 is an empty call and returns HV_OK without launching.
  * Errors: HV_ERR_INVALID_ARG, HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
 int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                            const int32_t* text_valid_len, hv_bf16* out,
                            const hv_layout* layout, int64_t n_video,
-                           float softmax_scale, void* stream);
+                           float softmax_scale, void* workspace,
+                           int64_t workspace_bytes, void* stream);
 
 /* hv_attention_fwd_lse: attention of query rows against a separate K/V
  * block, with the log-sum-exp of every row, for sequence-parallel (ring)
@@ -176,13 +200,15 @@ int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
  *   kv_valid_len  HOST array [batch] in [1, kv seq_len]; NULL = all keys
  *   lse           device fp32 [batch][24][q seq_len], 4-byte aligned,
  *                 disjoint from the tensors; NULL to skip
- *   softmax_scale as in hv_joint_attention_fwd
+ *   softmax_scale, workspace, workspace_bytes  as in hv_joint_attention_fwd
  * Errors: HV_ERR_INVALID_ARG (NULL, batch mismatch, valid length out of
- * range, alignment, overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+ * range, alignment, overlap, workspace too small), HV_ERR_UNSUPPORTED,
+ * HV_ERR_HIP. */
 int hv_attention_fwd_lse(const hv_bf16* q, const hv_layout* q_layout,
                          const hv_bf16* k, const hv_bf16* v, const hv_layout* kv_layout,
                          const int32_t* kv_valid_len, hv_bf16* out, float* lse,
-                         float softmax_scale, void* stream);
+                         float softmax_scale, void* workspace, int64_t workspace_bytes,
+                         void* stream);
 
 /* hv_attention_merge: combine n_parts attention results computed over
  * disjoint key blocks (e.g. by hv_attention_fwd_lse on each block of a ring)
@@ -217,13 +243,14 @@ int hv_attention_merge(const hv_bf16* const* outs, const float* const* lses,
  *   n_segments      1 .. HV_MAX_SEGMENTS
  *   lse             device fp32 [24][T] (natural-log log-sum-exp per row) or
  *                   NULL; rows outside every segment are not written
+ *   workspace, workspace_bytes  as in hv_joint_attention_fwd
  * Errors: HV_ERR_INVALID_ARG (NULL, batch != 1, bad offsets, alignment,
- * overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
+ * overlap, workspace too small), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
 int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                   int32_t n_segments, hv_bf16* out, float* lse,
                                   const hv_layout* layout, float softmax_scale,
-                                  void* stream);
+                                  void* workspace, int64_t workspace_bytes, void* stream);
 
 /* hv_joint_attention_bwd: gradients of hv_joint_attention_fwd by the chain
  * rule through the softmax (the training-side attention cost the report

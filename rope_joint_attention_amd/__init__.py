@@ -10,8 +10,9 @@ not built, every call raises (there is no fallback).
     hv_rope3d_apply(q, k, grid, theta)          # in place on video rows
     hv_qk_norm_rope3d_apply(q, k, grid, theta, gamma_q, gamma_k,
                             gamma_q_text=None, gamma_k_text=None, eps=1e-6)
+    hv_attention_workspace_bytes(n_keys, n_segments) -> int
     hv_joint_attention_fwd(q, k, v, text_valid_len, n_video, out=None,
-                           softmax_scale=None) -> out
+                           softmax_scale=None, workspace=None, pack_v=True) -> out
     hv_attention_fwd_lse(q, k, v, kv_valid_len=None, ...) -> (out, lse)
     hv_attention_merge(outs, lses, ...) -> (out, lse)
     hv_joint_attention_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k=None,
@@ -29,7 +30,8 @@ from typing import Optional, Sequence
 
 __all__ = [
     "HV_HEADS", "HV_HEAD_DIM", "HV_MAX_BATCH", "HvError", "HvGrid",
-    "hv_token_grid", "hv_rope3d_apply", "hv_qk_norm_rope3d_apply", "hv_joint_attention_fwd",
+    "hv_token_grid", "hv_rope3d_apply", "hv_qk_norm_rope3d_apply", "hv_attention_workspace_bytes",
+    "hv_joint_attention_fwd",
     "hv_attention_fwd_lse", "hv_attention_merge", "hv_joint_attention_varlen_fwd",
     "hv_joint_attention_bwd", "hv_joint_attention_varlen_bwd",
     "hv_status_string", "library_path", "load_library",
@@ -113,12 +115,15 @@ def load_library():
     lib.hv_joint_attention_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p,
                                            ctypes.POINTER(_Layout), ctypes.c_int64, ctypes.c_float,
-                                           ctypes.c_void_p]
+                                           ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.hv_joint_attention_fwd.restype = ctypes.c_int
+    lib.hv_attention_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    lib.hv_attention_workspace_bytes.restype = ctypes.c_int64
     lib.hv_attention_fwd_lse.argtypes = [ctypes.c_void_p, ctypes.POINTER(_Layout), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.POINTER(_Layout),
                                          ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p,
-                                         ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p]
+                                         ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_void_p]
     lib.hv_attention_fwd_lse.restype = ctypes.c_int
     lib.hv_attention_merge.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -129,7 +134,7 @@ def load_library():
                                                   ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                                   ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.POINTER(_Layout), ctypes.c_float,
-                                                  ctypes.c_void_p]
+                                                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.hv_joint_attention_varlen_fwd.restype = ctypes.c_int
     lib.hv_joint_attention_bwd.argtypes = [ctypes.c_void_p] * 6 + [
         ctypes.POINTER(ctypes.c_int32), ctypes.c_int64] + [ctypes.c_void_p] * 4 + [
@@ -230,9 +235,36 @@ def hv_qk_norm_rope3d_apply(q, k, grid: HvGrid, theta: float, gamma_q, gamma_k,
         raise HvError(st, "hv_qk_norm_rope3d_apply")
 
 
+def hv_attention_workspace_bytes(n_keys: int, n_segments: int) -> int:
+    """Upper bound of the packed-V workspace of a forward call (see hvattn.h)."""
+    return int(load_library().hv_attention_workspace_bytes(int(n_keys), int(n_segments)))
+
+
+def _workspace(workspace, pack_v: bool, nbytes: int, device):
+    """(pointer, bytes) of the packed-V workspace: the given tensor, a fresh
+    one of nbytes from torch's allocator, or (None, 0) for the in-place path."""
+    import torch
+
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if not pack_v:
+        return None, 0
+    # torch's allocator hands the block to later allocations on the same
+    # stream only, which run after this call's kernels: freeing it when this
+    # function returns is safe
+    ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device=device)
+    return ws.data_ptr(), nbytes
+
+
 def hv_joint_attention_fwd(q, k, v, text_valid_len: Optional[Sequence[int]], n_video: int,
-                           out=None, softmax_scale: Optional[float] = None):
-    """Joint [video; text] attention forward (see hvattn.h); returns out."""
+                           out=None, softmax_scale: Optional[float] = None, workspace=None,
+                           pack_v: bool = True):
+    """Joint [video; text] attention forward (see hvattn.h); returns out.
+    workspace: device tensor for the packed V (hv_attention_workspace_bytes
+    (batch * seq_len, batch) bytes); by default one is taken from torch's
+    allocator; pack_v=False (and no workspace) reads V in place."""
     import torch
 
     lay = _layout_of(q, "q")
@@ -250,9 +282,12 @@ def hv_joint_attention_fwd(q, k, v, text_valid_len: Optional[Sequence[int]], n_v
             raise ValueError("text_valid_len needs one entry per batch element")
         valid_arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    wptr, wbytes = _workspace(workspace, pack_v,
+                              hv_attention_workspace_bytes(q.shape[0] * q.shape[1], q.shape[0]),
+                              q.device)
     st = load_library().hv_joint_attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), valid_arr,
                                                out.data_ptr(), ctypes.byref(lay), int(n_video),
-                                               scale, _stream_of(q))
+                                               scale, wptr, wbytes, _stream_of(q))
     if st != HV_OK:
         raise HvError(st, "hv_joint_attention_fwd")
     return out
@@ -270,11 +305,13 @@ def _lse_buffer(lse, shape, device, what: str):
 
 
 def hv_attention_fwd_lse(q, k, v, kv_valid_len: Optional[Sequence[int]] = None, out=None,
-                         lse=None, want_lse: bool = True, softmax_scale: Optional[float] = None):
+                         lse=None, want_lse: bool = True, softmax_scale: Optional[float] = None,
+                         workspace=None, pack_v: bool = True):
     """Attention of q's rows against a separate K/V block, with the natural-log
     log-sum-exp of every row (see hvattn.h).  q: [B, Lq, 24, 128], k and v:
     [B, Lk, 24, 128] (sharing shape and strides).  Returns (out, lse) with lse
-    float32 [B, 24, Lq] (None when want_lse is False and no lse is given)."""
+    float32 [B, 24, Lq] (None when want_lse is False and no lse is given).
+    workspace / pack_v as in hv_joint_attention_fwd (n_keys = B * Lk)."""
     import torch
 
     qlay = _layout_of(q, "q")
@@ -294,10 +331,13 @@ def hv_attention_fwd_lse(q, k, v, kv_valid_len: Optional[Sequence[int]] = None, 
             raise ValueError("kv_valid_len needs one entry per batch element")
         valid_arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    wptr, wbytes = _workspace(workspace, pack_v,
+                              hv_attention_workspace_bytes(k.shape[0] * k.shape[1], k.shape[0]),
+                              q.device)
     st = load_library().hv_attention_fwd_lse(q.data_ptr(), ctypes.byref(qlay), k.data_ptr(),
                                              v.data_ptr(), ctypes.byref(kvlay), valid_arr,
                                              out.data_ptr(), None if lse is None else lse.data_ptr(),
-                                             scale, _stream_of(q))
+                                             scale, wptr, wbytes, _stream_of(q))
     if st != HV_OK:
         raise HvError(st, "hv_attention_fwd_lse")
     return out, lse
@@ -337,11 +377,13 @@ def hv_attention_merge(outs, lses, out=None, lse_out=None, want_lse: bool = True
 
 def hv_joint_attention_varlen_fwd(q, k, v, cu_seqlens_q: Sequence[int],
                                   cu_seqlens_k: Optional[Sequence[int]] = None, out=None, lse=None,
-                                  want_lse: bool = False, softmax_scale: Optional[float] = None):
+                                  want_lse: bool = False, softmax_scale: Optional[float] = None,
+                                  workspace=None, pack_v: bool = True):
     """Attention over packed segments (see hvattn.h).  q, k, v: [T, 24, 128]
     packed rows sharing shape and strides; cu_seqlens_*: segment offsets
     (cu_seqlens_k defaults to cu_seqlens_q).  Returns (out, lse) with lse
-    float32 [24, T] or None."""
+    float32 [24, T] or None.  workspace / pack_v as in hv_joint_attention_fwd
+    (n_keys = T)."""
     import torch
 
     def as4(t, name):
@@ -367,10 +409,13 @@ def hv_joint_attention_varlen_fwd(q, k, v, cu_seqlens_q: Sequence[int],
     aq = (ctypes.c_int32 * len(cq))(*cq)
     ak = (ctypes.c_int32 * len(ck))(*ck)
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    wptr, wbytes = _workspace(workspace, pack_v,
+                              hv_attention_workspace_bytes(q.shape[0], len(cq) - 1), q.device)
     st = load_library().hv_joint_attention_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), aq, ak,
                                                       len(cq) - 1, out.data_ptr(),
                                                       None if lse is None else lse.data_ptr(),
-                                                      ctypes.byref(lay), scale, _stream_of(q))
+                                                      ctypes.byref(lay), scale, wptr, wbytes,
+                                                      _stream_of(q))
     if st != HV_OK:
         raise HvError(st, "hv_joint_attention_varlen_fwd")
     return out, lse

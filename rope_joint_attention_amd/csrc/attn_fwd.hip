@@ -34,15 +34,19 @@
 //       which keeps every probability <= 256 and the result exact while
 //       skipping almost all accumulator rescales;
 //   O^T (128 channels x 32 queries) += V^T_tile * P^T -- P^T stays in the
-//       registers the softmax produced (bf16); V stays in its natural
-//       [key][channel] layout in LDS and the MFMA operand is gathered with
-//       the gfx950 transposing read ds_read_b64_tr_b16 (two per operand).
+//       registers the softmax produced (bf16).  The V^T operand wants 8 keys
+//       of one channel per lane.  With a workspace, V is first packed
+//       channel-major tile by tile (v_pack.hip) and each operand is one
+//       16-byte LDS read; without one, V stays in its natural [key][channel]
+//       layout and the operand is gathered with the gfx950 transposing read
+//       ds_read_b64_tr_b16 (two per operand, half the LDS read rate).
 //   The step is software-pipelined: the QK^T MFMAs of tile t+1 run under the
 //   softmax VALU work of tile t, the PV MFMAs of tile t under the row maximum
 //   of tile t+1.
 // LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled within a row (K:
 // slot c ^ (r % 16), V: slot c ^ 4(r % 4)) so that both the K operand reads
-// and the transposing V reads run without bank conflicts.  The padded-key
+// and the transposing V reads run without bank conflicts.  A packed V tile has
+// 128 rows of 128 bytes (one per channel) with slot c ^ ((r / 2) % 8).  The padded-key
 // mask is a loop bound plus a predicate on the last tile.  Rows past the
 // valid keys are never read: their loads are clamped to the last valid row,
 // whose scores are masked to -inf (K) or whose weights are exactly zero (V),
@@ -92,9 +96,14 @@ __device__ __forceinline__ int kswz(int r, int c) { return r * ROWB + ((c ^ (r &
 // exactly twice, the minimum for 512 bytes.
 __device__ __forceinline__ int vswz(int r, int c) { return r * ROWB + ((c ^ ((r & 3) << 2)) << 4); }
 
+// Maximum that propagates NaN (IEEE maximum): it lowers to gfx950's
+// v_maximum3_f32 with no input quieting, unlike fmaxf.  Scores are never NaN
+// unless an input is, and then the row's output is NaN either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float max_across_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_across_halves(float x) {
@@ -137,9 +146,9 @@ constexpr int kSchedDSRead = 0x100;
 // Row maximum of a score tile (32 in-lane values, then across the two halves),
 // in the log2 domain.  Masked keys must already be -inf.
 __device__ __forceinline__ float tile_max(const f32x16& s0, const f32x16& s1, float c2) {
-  float mx = fmaxf(s0[0], s1[0]);
+  float mx = vmax(s0[0], s1[0]);
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+  for (int v = 1; v < 16; ++v) mx = vmax(vmax(mx, s0[v]), s1[v]);
   return max_across_halves(mx) * c2;
 }
 
@@ -169,6 +178,7 @@ __device__ __forceinline__ void update_reference(float mx, float& m_run, float& 
   }
 }
 
+template <bool kPackedV>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // One LDS array per stage: with every access naming its array at compile
   // time, the compiler can tell the tile being loaded from the tiles being
@@ -222,6 +232,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const int64_t sl = p.kv_sl;
   const uint16_t* Kg = p.k + sg.k_off + (int64_t)head * D;
   const uint16_t* Vg = p.v + sg.k_off + (int64_t)head * D;
+  const int ntiles = (Lk + BN - 1) / BN;
+  // packed V: this head's tiles, 16 KB apart
+  const uint16_t* Vt = kPackedV ? p.vt + sg.vt_off + (int64_t)head * ntiles * kVtTileElems : nullptr;
 
   // Q^T operand: lane holds query row q0 + l32, channels 16*kc + 8*hh .. +7.
   const int q0 = qb * BM + wave * QPW;
@@ -260,7 +273,22 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     __builtin_amdgcn_global_load_lds(tb + o1, (HV_LDS void*)(dst + 1024), 16, 0, 0);
   };
   auto load_k = [&](auto st, int tile) { load_tile(Kg, kbuf(st), tile, lk0, lk1, ld_kc0, ld_kc1); };
-  auto load_v = [&](auto st, int tile) { load_tile(Vg, vbuf(st), tile, lv0, lv1, ld_vc, ld_vc); };
+  // Packed V tile: 128 rows of 128 bytes, instruction i = 2w + j covers rows
+  // 8i .. 8i+7; lane l fills slot l%8 of row 8i + l/8 with the chunk the
+  // row's swizzle (slot c ^ ((row / 2) % 8)) puts there.  Full tiles only:
+  // keys past the end are zeros in the workspace.
+  const uint32_t lt0 = (16 * wave + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 4)) << 4);
+  const uint32_t lt1 = (16 * wave + 8 + (lane >> 3)) * 128 + (((lane & 7) ^ (4 + (lane >> 4))) << 4);
+  auto load_v = [&](auto st, int tile) {
+    if constexpr (kPackedV) {
+      const unsigned char* tb = (const unsigned char*)(Vt + (int64_t)tile * kVtTileElems);
+      unsigned char* dst = vbuf(st) + wave * 2048;
+      __builtin_amdgcn_global_load_lds(tb + lt0, (HV_LDS void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(tb + lt1, (HV_LDS void*)(dst + 1024), 16, 0, 0);
+    } else {
+      load_tile(Vg, vbuf(st), tile, lv0, lv1, ld_vc, ld_vc);
+    }
+  };
 
   // Operand offsets inside a tile.  The swizzle only depends on the row modulo
   // 16, so moving 16 rows (V key groups) or 32 rows (K halves) is a plain
@@ -271,40 +299,55 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) koff[kc] = kswz(l32, 2 * kc + hh);
   // V^T operand for channels 32dt + l32 and keys 16mm + 8(e/4) + 4hh + e%4
-  // (slot e), matching the register layout of P^T.  ds_read_b64_tr_b16: in each
-  // group of 16 lanes, lane j receives element j%4 of the 8-byte rows that
-  // lanes j/4, j/4+4, j/4+8, j/4+12 address.  Lane p of a group addresses key
-  // (base + p/4), channels d0 + 4(p%4) .. +3, so lane j ends up with channel
-  // d0 + j of keys base .. base+3.
-  int voff[8];
-  {
+  // (slot e), matching the register layout of P^T.  The offsets include the
+  // LDS address of the first V stage (the V stages lie above 64 KB), so that
+  // stage and dt/mm offsets fold into the instruction's offset field.
+  const int vbase = (int)(uint32_t)(uintptr_t)(HV_LDS unsigned char*)sV0;
+  int voff[4];
+  if constexpr (kPackedV) {
+    // packed tile: row 32dt + l32, 16-byte chunk 2mm + hh (positions 16mm + 8hh
+    // .. +7, i.e. exactly the slot-e keys above) at slot (2mm + hh) ^ ((l32 / 2) % 8);
+    // dt moves 32 rows = 4 KB, an immediate
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) voff[mm] = vbase + l32 * 128 + (((2 * mm + hh) ^ ((l32 >> 1) & 7)) << 4);
+  } else {
+    // ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives element
+    // j%4 of the 8-byte rows that lanes j/4, j/4+4, j/4+8, j/4+12 address.
+    // Lane p of a group addresses key (base + p/4), channels d0 + 4(p%4) ..
+    // +3, so lane j ends up with channel d0 + j of keys base .. base+3.  Keys 8
+    // further are 8 rows = 2 KB further with the same swizzle (an immediate);
+    // only dt changes the swizzled slot.
     const int tr_key = 4 * hh + ((lane & 15) >> 2);
     const int tr_ch = 16 * ((lane & 31) >> 4) + 4 * (lane & 3);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int ch = 32 * dt + tr_ch;
-        voff[2 * dt + q] = vswz(tr_key + 8 * q, ch >> 3) + 2 * (ch & 7);
-      }
+    for (int dt = 0; dt < 4; ++dt) {
+      const int ch = 32 * dt + tr_ch;
+      voff[dt] = vbase + vswz(tr_key, ch >> 3) + 2 * (ch & 7);
+    }
   }
   // Re-declared opaque once per step, so the compiler keeps the 16 offsets in
   // registers and folds array base + stage-free immediates into the ds_read
   // offset fields, instead of hoisting every (offset + immediate) sum.
   auto refresh_offsets = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(koff[i]), "+v"(voff[i]));
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(koff[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(voff[i]));
   };
   auto k_frag = [&](auto st, int half, int kc) {
     return *reinterpret_cast<const bf16x8*>(kbuf(st) + koff[kc] + half * 32 * ROWB);
   };
   auto v_frag = [&](auto st, int dt, int mm) {
-    unsigned char* vb = vbuf(st);
-    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(vb + voff[2 * dt] + mm * 16 * ROWB));
-    const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(vb + voff[2 * dt + 1] + mm * 16 * ROWB));
-    const u32x4 w = {__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1],
-                     __builtin_bit_cast(u32x2, c)[0], __builtin_bit_cast(u32x2, c)[1]};
-    return __builtin_bit_cast(bf16x8, w);
+    unsigned char* vb = vbuf(st) - vbase;
+    if constexpr (kPackedV) {
+      return *(const HV_LDS bf16x8*)(HV_LDS unsigned char*)(vb + voff[mm] + dt * 32 * 128);
+    } else {
+      const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(vb + voff[dt] + mm * 16 * ROWB));
+      const i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HV_LDS i16x4*)(vb + voff[dt] + 8 * ROWB + mm * 16 * ROWB));
+      const u32x4 w = {__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1],
+                       __builtin_bit_cast(u32x2, c)[0], __builtin_bit_cast(u32x2, c)[1]};
+      return __builtin_bit_cast(bf16x8, w);
+    }
   };
 
   f32x16 o[4];
@@ -315,7 +358,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   float m_run = -INFINITY;  // running reference, log2 domain
   float l_run = 0.f;        // this lane's share of the denominator (bf16-rounded weights)
   const float c2 = p.scale_log2;
-  const int ntiles = (Lk + BN - 1) / BN;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
@@ -428,9 +470,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       }
       if (i >= 8 && i < 12) {  // row maximum of tile t+1, in four slices
         const int j = i - 8;
-        float m = fmaxf(nxt[j >> 1][8 * (j & 1)], nxt[j >> 1][8 * (j & 1) + 1]);
+        float m = vmax(nxt[j >> 1][8 * (j & 1)], nxt[j >> 1][8 * (j & 1) + 1]);
 #pragma unroll
-        for (int v = 2; v < 8; ++v) m = fmaxf(m, nxt[j >> 1][8 * (j & 1) + v]);
+        for (int v = 2; v < 8; ++v) m = vmax(m, nxt[j >> 1][8 * (j & 1) + v]);
         part[j] = m;
       }
     }
@@ -442,7 +484,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     __builtin_amdgcn_sched_barrier(0);
     load_k(KL{}, min(t + KAHEAD, ntiles - 1));
     load_v(VL{}, min(t + VAHEAD, ntiles - 1));
-    const float mx = max_across_halves(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]))) * c2;
+    const float mx = max_across_halves(vmax(vmax(part[0], part[1]), vmax(part[2], part[3]))) * c2;
     barrier_after<4>();  // the 4 loads just issued stay in flight
     update_reference(mx, m_run, l_run, o);
   };
@@ -518,15 +560,40 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
 
 hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream) {
   int blocks = 0;
+  int64_t vt_elems = 0;
+  VtParams vp;
+  vp.v = p.v;
+  vp.vt = p.vt;
+  vp.kv_sl = p.kv_sl;
+  vp.n_seg = p.n_seg;
+  vp.n_blocks = 0;
   for (int i = 0; i < p.n_seg; ++i) {
     AttnSegment& sg = p.seg[i];
     sg.nqb = (sg.q_len + BM - 1) / BM;
     sg.blk_begin = blocks;
     blocks += HV_HEADS * sg.nqb;
+    // packed V only for segments with query rows
+    const int nt = sg.q_len > 0 ? (sg.k_len + BN - 1) / BN : 0;
+    sg.vt_off = vt_elems;
+    VtSegment& vs = vp.seg[i];
+    vs.k_off = sg.k_off;
+    vs.vt_off = vt_elems;
+    vs.k_len = sg.k_len;
+    vs.ntiles = nt;
+    vs.blk_begin = vp.n_blocks;
+    vs.pad_ = 0;
+    vp.n_blocks += HV_HEADS * nt;
+    vt_elems += (int64_t)HV_HEADS * nt * kVtTileElems;
   }
   p.n_blocks = blocks;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+  if (p.vt != nullptr) {
+    const hipError_t e = launch_v_pack(vp, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

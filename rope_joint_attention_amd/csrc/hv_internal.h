@@ -69,11 +69,26 @@ struct AttnSegment {
   int64_t k_off;     // elements (k and v)
   int64_t o_off;     // elements
   int64_t lse_off;   // index of (head 0, row 0) in lse
+  int64_t vt_off;    // elements: the segment's packed V in the workspace
   int32_t q_len;     // query rows
   int32_t k_len;     // keys, >= 1 when q_len > 0
   int32_t blk_begin; // first logical block
   int32_t nqb;       // query blocks per head
 };
+
+// Packed V (optional workspace): for every segment with query rows, head h
+// and 64-key tile t, a contiguous 16 KB block at
+//   vt + vt_off + (h * ntiles + t) * 8192 elements,  ntiles = ceil(k_len / 64),
+// holding the tile channel-major: row d (0..127) is 64 bf16, position p of
+// the row is key 64t + kv_key_of_pos(p) of channel d; keys >= k_len are 0.
+// Inside each group of 16 keys the positions swap bits 2 and 3 of the key
+// index, which puts the 8 keys one lane needs for an MFMA operand (the order
+// the probabilities come out of the score MFMA) next to each other.
+constexpr int kVtTileElems = 64 * HV_HEAD_DIM;  // 8192 elements = 16 KB
+
+__host__ __device__ constexpr int kv_key_of_pos(int p) {
+  return (p & ~15) | (p & 3) | (((p >> 3) & 1) << 2) | (((p >> 2) & 1) << 3);
+}
 
 struct AttnParams {
   const uint16_t* q;
@@ -81,6 +96,7 @@ struct AttnParams {
   const uint16_t* v;
   uint16_t* out;
   float* lse;          // natural-log log-sum-exp per (head, row); may be null
+  uint16_t* vt;        // packed V workspace; null: V is read in place
   int64_t q_sl;        // token strides, elements
   int64_t kv_sl;
   int64_t o_sl;
@@ -92,8 +108,39 @@ struct AttnParams {
   AttnSegment seg[kMaxSegments];
 };
 
-// Fills blk_begin / nqb / n_blocks from q_len and launches.
+// Bytes of packed V that the segments of p need (segments without query rows
+// need none).
+inline int64_t attn_workspace_bytes(const AttnParams& p) {
+  int64_t tiles = 0;
+  for (int i = 0; i < p.n_seg; ++i)
+    if (p.seg[i].q_len > 0) tiles += (p.seg[i].k_len + 63) / 64;
+  return tiles * HV_HEADS * kVtTileElems * 2;
+}
+
+// Fills blk_begin / nqb / n_blocks from q_len (and vt_off when p.vt is set),
+// packs V into p.vt when it is set, and launches the attention.
 hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream);
+
+// ---- V packing for the attention forward --------------------------------------
+struct VtSegment {
+  int64_t k_off;     // elements of v
+  int64_t vt_off;    // elements of vt
+  int32_t k_len;
+  int32_t ntiles;    // ceil(k_len / 64)
+  int32_t blk_begin; // first block: blocks run head-major over the tiles
+  int32_t pad_;
+};
+
+struct VtParams {
+  const uint16_t* v;
+  uint16_t* vt;
+  int64_t kv_sl;       // token stride of v, elements
+  int32_t n_seg;
+  int32_t n_blocks;
+  VtSegment seg[kMaxSegments];
+};
+
+hipError_t launch_v_pack(const VtParams& p, hipStream_t stream);
 
 // ---- merge of partial attention results -------------------------------------
 // n_parts outputs over disjoint key blocks (same layout as out) and their
@@ -163,5 +210,6 @@ hipError_t launch_attn_bwd(BwdParams& p, hipStream_t stream);
 static_assert(sizeof(AttnParams) <= 4096, "attention kernel arguments exceed 4 KB");
 static_assert(sizeof(BwdParams) <= 4096, "backward kernel arguments exceed 4 KB");
 static_assert(sizeof(MergeParams) <= 4096, "merge kernel arguments exceed 4 KB");
+static_assert(sizeof(VtParams) <= 4096, "V packing kernel arguments exceed 4 KB");
 
 }  // namespace hv

@@ -72,6 +72,19 @@ bool overlap_any(const void* a, int64_t ea, const void* b, int64_t eb, const hv_
   return same ? overlap(a, b, la, ea) : true;
 }
 
+// The packed-V workspace of a forward call: enough bytes for the segments of
+// p, 16-byte aligned and disjoint from the n byte ranges [ptr, ptr + len).
+// A NULL workspace selects the in-place V path and needs nothing.
+int check_workspace(const hv::AttnParams& p, const void* ws, int64_t ws_bytes,
+                    const void* const* ptrs, const uintptr_t* lens, int n) {
+  if (ws_bytes < 0) return HV_ERR_INVALID_ARG;
+  if (ws == nullptr) return HV_OK;
+  if (!aligned16(ws) || ws_bytes < hv::attn_workspace_bytes(p)) return HV_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (ptrs[i] && ranges_meet(ws, (uintptr_t)ws_bytes, ptrs[i], lens[i])) return HV_ERR_INVALID_ARG;
+  return HV_OK;
+}
+
 float scale_log2(float softmax_scale) {
   float scale = softmax_scale;
   if (!(scale > 0.f) || !isfinite(scale)) scale = 1.0f / sqrtf((float)HV_HEAD_DIM);
@@ -158,7 +171,13 @@ void rope_frequencies(float theta, float* freq) {
 
 extern "C" {
 
-int hv_version(void) { return 10000; }
+int hv_version(void) { return 10100; }
+
+int64_t hv_attention_workspace_bytes(int64_t n_keys, int32_t n_segments) {
+  if (n_keys < 0 || n_segments < 0) return 0;
+  const int64_t tiles = (n_keys + 63 * (int64_t)n_segments) / 64;
+  return tiles * HV_HEADS * hv::kVtTileElems * 2;
+}
 
 const char* hv_status_string(int status) {
   switch (status) {
@@ -276,7 +295,7 @@ int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout, con
 int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                            const int32_t* text_valid_len, hv_bf16* out,
                            const hv_layout* layout, int64_t n_video, float softmax_scale,
-                           void* stream) {
+                           void* workspace, int64_t workspace_bytes, void* stream) {
   int64_t extent = 0;
   int st = check_layout(layout, &extent);
   if (st != HV_OK) return st;
@@ -301,10 +320,18 @@ int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
     sg.k_len = (int32_t)(n_video + valid);
   }
   p.n_seg = layout->batch;
+  {
+    const void* ptrs[4] = {q, k, v, out};
+    const uintptr_t n = (uintptr_t)extent * 2;
+    const uintptr_t lens[4] = {n, n, n, n};
+    st = check_workspace(p, workspace, workspace_bytes, ptrs, lens, 4);
+    if (st != HV_OK) return st;
+  }
   p.q = q;
   p.k = k;
   p.v = v;
   p.out = out;
+  p.vt = (uint16_t*)workspace;
   p.q_sl = p.kv_sl = p.o_sl = layout->stride_l;
   p.scale_log2 = scale_log2(softmax_scale);
   const hipError_t e = hv::launch_attn_fwd(p, (hipStream_t)stream);
@@ -314,7 +341,8 @@ int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
 int hv_attention_fwd_lse(const hv_bf16* q, const hv_layout* q_layout, const hv_bf16* k,
                          const hv_bf16* v, const hv_layout* kv_layout,
                          const int32_t* kv_valid_len, hv_bf16* out, float* lse,
-                         float softmax_scale, void* stream) {
+                         float softmax_scale, void* workspace, int64_t workspace_bytes,
+                         void* stream) {
   int64_t qext = 0, kvext = 0;
   int st = check_layout(q_layout, &qext);
   if (st != HV_OK) return st;
@@ -350,11 +378,19 @@ int hv_attention_fwd_lse(const hv_bf16* q, const hv_layout* q_layout, const hv_b
     sg.k_len = (int32_t)n;
   }
   p.n_seg = B;
+  {
+    const void* ptrs[5] = {q, k, v, out, lse};
+    const uintptr_t lens[5] = {(uintptr_t)qext * 2, (uintptr_t)kvext * 2, (uintptr_t)kvext * 2,
+                               (uintptr_t)qext * 2, (uintptr_t)B * HV_HEADS * Lq * sizeof(float)};
+    st = check_workspace(p, workspace, workspace_bytes, ptrs, lens, 5);
+    if (st != HV_OK) return st;
+  }
   p.q = q;
   p.k = k;
   p.v = v;
   p.out = out;
   p.lse = lse;
+  p.vt = (uint16_t*)workspace;
   p.q_sl = p.o_sl = q_layout->stride_l;
   p.kv_sl = kv_layout->stride_l;
   p.lse_hstride = Lq;
@@ -366,7 +402,8 @@ int hv_attention_fwd_lse(const hv_bf16* q, const hv_layout* q_layout, const hv_b
 int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                   int32_t n_segments, hv_bf16* out, float* lse,
-                                  const hv_layout* layout, float softmax_scale, void* stream) {
+                                  const hv_layout* layout, float softmax_scale, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
   int64_t extent = 0;
   int st = check_layout(layout, &extent);
   if (st != HV_OK) return st;
@@ -403,11 +440,19 @@ int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_b
   }
   if (T == 0) return HV_OK;
   p.n_seg = n_segments;
+  {
+    const void* ptrs[5] = {q, k, v, out, lse};
+    const uintptr_t n = (uintptr_t)extent * 2;
+    const uintptr_t lens[5] = {n, n, n, n, (uintptr_t)HV_HEADS * T * sizeof(float)};
+    st = check_workspace(p, workspace, workspace_bytes, ptrs, lens, 5);
+    if (st != HV_OK) return st;
+  }
   p.q = q;
   p.k = k;
   p.v = v;
   p.out = out;
   p.lse = lse;
+  p.vt = (uint16_t*)workspace;
   p.q_sl = p.kv_sl = p.o_sl = layout->stride_l;
   p.lse_hstride = T;
   p.scale_log2 = scale_log2(softmax_scale);

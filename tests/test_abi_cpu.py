@@ -113,12 +113,12 @@ def rope(q=FAKE, k=FAKE + SEP, lay=None, g=None, theta=10000.0):
 
 
 def attn(q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP, out=FAKE + 3 * SEP, valid=(10,), lay=None,
-         n_video=40, scale=0.0):
+         n_video=40, scale=0.0, ws=None, ws_bytes=0):
     lib = hv.load_library()
     lay = layout() if lay is None else lay
     arr = None if valid is None else (ctypes.c_int32 * max(1, len(valid)))(*valid)
     return lib.hv_joint_attention_fwd(q, k, v, arr, out, ctypes.byref(lay) if lay is not False else None,
-                                      n_video, scale, None)
+                                      n_video, scale, ws, ws_bytes, None)
 
 
 E, U = hv.HV_ERR_INVALID_ARG, hv.HV_ERR_UNSUPPORTED
@@ -252,14 +252,14 @@ LSE = FAKE + 8 * SEP
 
 
 def attn_lse(q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP, out=FAKE + 3 * SEP, lse=LSE, valid=None,
-             qlay=None, kvlay=None, scale=0.0):
+             qlay=None, kvlay=None, scale=0.0, ws=None, ws_bytes=0):
     lib = hv.load_library()
     qlay = layout(seq=200) if qlay is None else qlay
     kvlay = layout(seq=300) if kvlay is None else kvlay
     arr = None if valid is None else (ctypes.c_int32 * max(1, len(valid)))(*valid)
     return lib.hv_attention_fwd_lse(q, ctypes.byref(qlay) if qlay is not False else None, k, v,
                                     ctypes.byref(kvlay) if kvlay is not False else None, arr, out,
-                                    lse, scale, None)
+                                    lse, scale, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kwargs,expect", [
@@ -320,14 +320,15 @@ def test_merge_accepts_16_parts_and_null_lse_out_when_empty():
 
 
 def varlen(cq=(0, 100, 300), ck=None, n=None, q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP,
-           out=FAKE + 3 * SEP, lse=LSE, lay=None):
+           out=FAKE + 3 * SEP, lse=LSE, lay=None, ws=None, ws_bytes=0):
     lib = hv.load_library()
     ck = cq if ck is None else ck
     n = len(cq) - 1 if n is None else n
     aq = (ctypes.c_int32 * len(cq))(*cq)
     ak = (ctypes.c_int32 * len(ck))(*ck)
     lay = layout() if lay is None else lay
-    return lib.hv_joint_attention_varlen_fwd(q, k, v, aq, ak, n, out, lse, ctypes.byref(lay), 0.0, None)
+    return lib.hv_joint_attention_varlen_fwd(q, k, v, aq, ak, n, out, lse, ctypes.byref(lay), 0.0,
+                                             ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kwargs,expect", [
@@ -415,3 +416,49 @@ def test_varlen_bwd_validation(kwargs, expect):
 
 def test_varlen_bwd_empty_segments_launch_nothing():
     assert varlen_bwd(cq=(0, 0, 0), ck=(0, 0, 0)) == hv.HV_OK
+
+
+# ------------------------------------------------- packed-V workspace (forward)
+WS = FAKE + 20 * SEP
+TILE_BYTES = 24 * 64 * 128 * 2      # one 64-key tile of packed V for all heads
+
+
+@pytest.mark.parametrize("n_keys,n_seg,tiles", [
+    (0, 0, 0), (1, 1, 1), (64, 1, 1), (65, 1, 2), (300, 1, 5), (119056, 1, 1861),
+    (2 * 300, 2, 11), (100, 3, 4), (-1, 1, 0), (5, -1, 0),   # floor((n + 63 s) / 64) tiles
+])
+def test_workspace_bytes(n_keys, n_seg, tiles):
+    assert hv.hv_attention_workspace_bytes(n_keys, n_seg) == tiles * TILE_BYTES
+
+
+def test_workspace_bound_covers_every_split():
+    # sum over segments of ceil(k / 64) never exceeds the bound for their total
+    import random
+    r = random.Random(5)
+    for _ in range(2000):
+        ks = [r.randint(0, 300) for _ in range(r.randint(1, 64))]
+        need = sum((k + 63) // 64 for k in ks) * TILE_BYTES
+        assert need <= hv.hv_attention_workspace_bytes(sum(ks), len(ks))
+
+
+# default attn(): one segment of 40 + 10 keys = 1 tile; attn_lse(): 300 keys = 5
+# tiles; varlen(): segments of 100 and 200 keys = 2 + 4 tiles
+@pytest.mark.parametrize("call,need", [(attn, TILE_BYTES), (attn_lse, 5 * TILE_BYTES),
+                                       (varlen, 6 * TILE_BYTES)])
+def test_workspace_validation(call, need):
+    assert call(ws=WS, ws_bytes=need - 1) == E                  # too small
+    assert call(ws=WS, ws_bytes=0) == E
+    assert call(ws=WS + 8, ws_bytes=need + 64) == E             # not 16-byte aligned
+    assert call(ws=WS, ws_bytes=-1) == E
+    assert call(ws=None, ws_bytes=-1) == E
+    assert call(ws=FAKE + 64, ws_bytes=need) == E               # inside q
+    assert call(ws=FAKE + SEP - 1024, ws_bytes=need) == E       # runs into k
+    assert call(ws=FAKE + 2 * SEP + 4096, ws_bytes=need) == E   # inside v
+    assert call(ws=FAKE + 3 * SEP, ws_bytes=need) == E          # is out
+
+
+def test_workspace_must_not_meet_lse():
+    need = 6 * TILE_BYTES
+    assert attn_lse(ws=LSE - 128, ws_bytes=5 * TILE_BYTES) == E
+    assert varlen(ws=LSE + 256, ws_bytes=need) == E
+

@@ -1,0 +1,190 @@
+"""GPU checks of the packed-V path of the attention forward calls.
+
+With a workspace, hv_joint_attention_fwd / hv_attention_fwd_lse /
+hv_joint_attention_varlen_fwd first rewrite V tile by tile channel-major into
+it and read each P V operand with one 16-byte LDS read; without one they read
+V in place with the transposing LDS read.  Both feed the same values into the
+same MFMA slots, so the outputs (and log-sum-exps) must agree bit for bit.
+
+* bitwise agreement of the two paths on small shapes around the 64-key tile
+  (ragged tails, one key, exact multiples of 64, batch entries with different
+  valid lengths), on the log-sum-exp form with its own K/V length, and on
+  packed segments with empty ones in between;
+* the workspace holds exactly the documented packed layout (per segment,
+  head and tile: 128 channel rows of 64 keys, keys swapped in bits 2 and 3
+  inside each group of 16, zeros past the valid keys) and nothing past the
+  bytes the call needs is written;
+* one workspace reused by two calls in a row, the second smaller; poisoned
+  padded rows never reach the workspace; a too-small workspace is refused.
+Parity with the fp64 oracle for the packed path is covered by every other GPU
+attention test, which run it by default.
+"""
+import numpy as np
+import pytest
+
+import hvinputs
+from hvtest_util import assert_close, bits_to_torch, log, torch_to_bits, widen
+from oracle import joint_attention
+
+pytestmark = pytest.mark.gpu
+
+TILE = 64 * 128  # elements of one (head, tile) block
+
+
+def key_of_pos(p):
+    p = np.asarray(p)
+    return (p & ~15) | (p & 3) | (((p >> 3) & 1) << 2) | (((p >> 2) & 1) << 3)
+
+
+def expected_packed(vbits, k_lens, k_offs):
+    """The packed layout for segments (k_off row, k_len) of v[rows, 24, 128]."""
+    blocks = []
+    pos = np.arange(64)
+    for k0, n in zip(k_offs, k_lens):
+        nt = (n + 63) // 64
+        for h in range(24):
+            for t in range(nt):
+                keys = 64 * t + key_of_pos(pos)
+                blk = np.zeros((128, 64), np.uint16)
+                ok = keys < n
+                blk[:, ok] = vbits[k0 + keys[ok], h, :].T
+                blocks.append(blk.reshape(-1))
+    return np.concatenate(blocks) if blocks else np.zeros(0, np.uint16)
+
+
+SHAPES = [
+    # batch, n_video, text capacity, valid text per batch entry
+    (1, 1, 0, [0]),            # one key
+    (1, 40, 24, [24]),         # exactly one tile
+    (1, 40, 25, [24]),         # 64 keys, one padded row
+    (2, 63, 2, [0, 2]),        # keys 63 and 65
+    (1, 200, 57, [13]),
+    (3, 300, 45, [45, 3, 0]),
+    (1, 2047, 256, [255]),
+]
+
+
+@pytest.mark.parametrize("B,n_video,cap,valid", SHAPES, ids=lambda x: str(x))
+def test_packed_and_inplace_paths_agree_bitwise(B, n_video, cap, valid):
+    import torch
+    import rope_joint_attention_amd as hv
+
+    L = n_video + cap
+    bits = hvinputs.draw_qkv(B, L, seed=31 * L + B)
+    q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
+    log(f"packed vs in-place B={B} N={n_video} L={L} valid={valid}")
+    a = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, pack_v=True)
+    b = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, pack_v=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch_to_bits(a), torch_to_bits(b))
+    ref = joint_attention(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), n_video, valid)
+    assert_close(widen(torch_to_bits(a)), ref, f"packed B={B} L={L}")
+
+
+def test_lse_form_agrees_bitwise():
+    import torch
+    import rope_joint_attention_amd as hv
+
+    bq = hvinputs.draw_qkv(2, 300, seed=91)
+    bk = hvinputs.draw_qkv(2, 517, seed=92)
+    q = bits_to_torch(bq["q"])
+    k, v = bits_to_torch(bk["k"]), bits_to_torch(bk["v"])
+    log("packed vs in-place: lse form, 300 queries x 517 keys, valid 517 / 130")
+    oa, la = hv.hv_attention_fwd_lse(q, k, v, [517, 130], pack_v=True)
+    ob, lb = hv.hv_attention_fwd_lse(q, k, v, [517, 130], pack_v=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(torch_to_bits(oa), torch_to_bits(ob))
+    assert np.array_equal(la.cpu().numpy().view(np.uint32), lb.cpu().numpy().view(np.uint32))
+
+
+def test_varlen_form_agrees_bitwise():
+    import torch
+    import rope_joint_attention_amd as hv
+
+    T = 700
+    bits = hvinputs.draw_qkv(1, T, seed=93)
+    q, k, v = (bits_to_torch(bits[n][0]) for n in ("q", "k", "v"))
+    cq = [0, 130, 130, 400, 650]
+    ck = [0, 200, 260, 300, 700]   # segment 1 has keys but no queries
+    log(f"packed vs in-place: varlen cu_q={cq} cu_k={ck}")
+    oa, la = hv.hv_joint_attention_varlen_fwd(q, k, v, cq, ck, want_lse=True, pack_v=True)
+    ob, lb = hv.hv_joint_attention_varlen_fwd(q, k, v, cq, ck, want_lse=True, pack_v=False)
+    torch.cuda.synchronize()
+    a, b = torch_to_bits(oa), torch_to_bits(ob)
+    assert np.array_equal(a[:650], b[:650])
+    la, lb = la.cpu().numpy(), lb.cpu().numpy()
+    assert np.array_equal(la[:, :650].view(np.uint32), lb[:, :650].view(np.uint32))
+
+
+def test_workspace_holds_the_packed_layout():
+    import torch
+    import rope_joint_attention_amd as hv
+
+    B, n_video, cap, valid = 2, 150, 40, [40, 7]     # 190 and 157 keys: 3 tiles each
+    L = n_video + cap
+    bits = hvinputs.draw_qkv(B, L, seed=94)
+    vb = bits["v"].copy()
+    vb[1, n_video + 7:] = 0x7FC0                     # NaN in the padded rows of entry 1
+    q, k, v = bits_to_torch(bits["q"]), bits_to_torch(bits["k"]), bits_to_torch(vb)
+    need = sum((n_video + x + 63) // 64 for x in valid) * 24 * TILE * 2
+    cap_bytes = hv.hv_attention_workspace_bytes(B * L, B)
+    assert cap_bytes >= need
+    ws = torch.full((cap_bytes // 2,), 0x1234, dtype=torch.int16, device="cuda")
+    log(f"packed layout B={B} L={L} valid={valid}: need {need} bytes of {cap_bytes}")
+    out = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, workspace=ws)
+    torch.cuda.synchronize()
+    got = ws.cpu().numpy().view(np.uint16)
+    want = np.concatenate([expected_packed(vb[b], [n_video + valid[b]], [0]) for b in range(B)])
+    assert want.size * 2 == need
+    assert np.array_equal(got[:want.size], want)
+    assert (got[want.size:] == 0x1234).all()          # nothing past what the call needs
+    o = widen(torch_to_bits(out))
+    assert np.isfinite(o).all()
+    ref = joint_attention(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), n_video, valid)
+    assert_close(o, ref, "packed layout call")
+
+
+def test_varlen_workspace_layout_skips_segments_without_queries():
+    import torch
+    import rope_joint_attention_amd as hv
+
+    T = 400
+    bits = hvinputs.draw_qkv(1, T, seed=95)
+    q, k, v = (bits_to_torch(bits[n][0]) for n in ("q", "k", "v"))
+    cq = [0, 100, 100, 300]
+    ck = [0, 70, 200, 330]          # segment 1: 130 keys, no queries -> not packed
+    ws = torch.zeros(hv.hv_attention_workspace_bytes(T, 3) // 2, dtype=torch.int16, device="cuda")
+    log("varlen packed layout with a query-less segment")
+    hv.hv_joint_attention_varlen_fwd(q, k, v, cq, ck, workspace=ws)
+    torch.cuda.synchronize()
+    got = ws.cpu().numpy().view(np.uint16)
+    want = expected_packed(bits["v"][0], [70, 130], [0, 200])
+    assert np.array_equal(got[:want.size], want)
+
+
+def test_workspace_reused_by_consecutive_calls():
+    import torch
+    import rope_joint_attention_amd as hv
+
+    ws = torch.empty(hv.hv_attention_workspace_bytes(1300, 1), dtype=torch.uint8, device="cuda")
+    for L, valid, seed in ((1300, [100], 96), (333, [17], 97)):
+        bits = hvinputs.draw_qkv(1, L, seed=seed)
+        q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
+        n_video = L - 120
+        log(f"workspace reuse L={L}")
+        a = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, workspace=ws)
+        b = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, pack_v=False)
+        torch.cuda.synchronize()
+        assert np.array_equal(torch_to_bits(a), torch_to_bits(b))
+
+
+def test_too_small_workspace_is_refused():
+    import torch
+    import rope_joint_attention_amd as hv
+
+    bits = hvinputs.draw_qkv(1, 200, seed=98)
+    q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
+    ws = torch.empty(4 * 24 * TILE * 2 - 16, dtype=torch.uint8, device="cuda")   # 4 tiles needed
+    with pytest.raises(hv.HvError) as ei:
+        hv.hv_joint_attention_fwd(q, k, v, [50], 150, workspace=ws)
+    assert ei.value.status == hv.HV_ERR_INVALID_ARG
