@@ -202,7 +202,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   using I3 = std::integral_constant<int, 3>;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index as a scalar: the LDS destinations of the tile loads (M0) are
+  // then computed on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Waves w and w+4 share a SIMD.  Fixed, unequal priorities let one of the
   // pair issue first whenever both are ready, so the other fills its stalls
   // instead of the two advancing in lockstep (measured: about 0.5 % faster).
@@ -266,21 +268,27 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     unsigned char* dst = buf + wave * 2048;
     if (tile * BN + BN > Lk) {  // partial last tile: clamp to the last valid row
       const int lim = Lk - 1 - tile * BN;
-      o0 = (uint32_t)min(ld_row0, lim) * row_bytes + c0 * 16;
-      o1 = (uint32_t)min(ld_row0 + 4, lim) * row_bytes + c1 * 16;
+      const uint32_t c0o = (uint32_t)min(ld_row0, lim) * row_bytes + c0 * 16;
+      const uint32_t c1o = (uint32_t)min(ld_row0 + 4, lim) * row_bytes + c1 * 16;
+      __builtin_amdgcn_global_load_lds(tb + c0o, (HV_LDS void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(tb + c1o, (HV_LDS void*)(dst + 1024), 16, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(tb + o0, (HV_LDS void*)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(tb + o1, (HV_LDS void*)(dst + 1024), 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds(tb + o0, (HV_LDS void*)dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(tb + o1, (HV_LDS void*)(dst + 1024), 16, 0, 0);
   };
   auto load_k = [&](auto st, int tile) { load_tile(Kg, kbuf(st), tile, lk0, lk1, ld_kc0, ld_kc1); };
   // Packed V tile: 128 rows of 128 bytes, instruction i = 2w + j covers rows
   // 8i .. 8i+7; lane l fills slot l%8 of row 8i + l/8 with the chunk the
   // row's swizzle (slot c ^ ((row / 2) % 8)) puts there.  Full tiles only:
   // keys past the end are zeros in the workspace.
-  const uint32_t lt0 = (16 * wave + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 4)) << 4);
-  const uint32_t lt1 = (16 * wave + 8 + (lane >> 3)) * 128 + (((lane & 7) ^ (4 + (lane >> 4))) << 4);
+  uint32_t lt0 = (16 * wave + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 4)) << 4);
+  uint32_t lt1 = (16 * wave + 8 + (lane >> 3)) * 128 + (((lane & 7) ^ (4 + (lane >> 4))) << 4);
   auto load_v = [&](auto st, int tile) {
     if constexpr (kPackedV) {
+      // opaque per call: keeps the scalar tile base + 32-bit lane offset form
+      // instead of 64-bit per-lane addresses hoisted out of the loop
+      asm volatile("" : "+v"(lt0), "+v"(lt1));
       const unsigned char* tb = (const unsigned char*)(Vt + (int64_t)tile * kVtTileElems);
       unsigned char* dst = vbuf(st) + wave * 2048;
       __builtin_amdgcn_global_load_lds(tb + lt0, (HV_LDS void*)dst, 16, 0, 0);
@@ -456,7 +464,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     bf16x8 vf[2];
     vf[0] = v_frag(VS{}, 0, 0);
     vf[1] = v_frag(VS{}, 1, 0);
-    float part[4];
+    float part_run = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -468,12 +476,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         if (i == 3) pb[2] = pack_p(cur, 2);
         if (i == 7) pb[3] = pack_p(cur, 3);
       }
-      if (i >= 8 && i < 12) {  // row maximum of tile t+1, in four slices
+      if (i >= 8 && i < 12) {  // row maximum of tile t+1, in four slices of one chain
         const int j = i - 8;
-        float m = vmax(nxt[j >> 1][8 * (j & 1)], nxt[j >> 1][8 * (j & 1) + 1]);
+        const f32x16& sv = nxt[j >> 1];
+        const int b = 8 * (j & 1);
+        float m = j ? vmax(vmax(part_run, sv[b]), sv[b + 1]) : vmax(sv[b], sv[b + 1]);
 #pragma unroll
-        for (int v = 2; v < 8; ++v) m = vmax(m, nxt[j >> 1][8 * (j & 1) + v]);
-        part[j] = m;
+        for (int v = 2; v < 8; v += 2) m = vmax(vmax(m, sv[b + v]), sv[b + v + 1]);
+        part_run = m;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -484,7 +494,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     __builtin_amdgcn_sched_barrier(0);
     load_k(KL{}, min(t + KAHEAD, ntiles - 1));
     load_v(VL{}, min(t + VAHEAD, ntiles - 1));
-    const float mx = max_across_halves(vmax(vmax(part[0], part[1]), vmax(part[2], part[3]))) * c2;
+    const float mx = max_across_halves(part_run) * c2;
     barrier_after<4>();  // the 4 loads just issued stay in flight
     update_reference(mx, m_run, l_run, o);
   };
