@@ -281,12 +281,15 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   // dK^T += Q^T dS (16 MFMAs).  The units are staggered so that the VALU work
   // of one runs under the MFMAs of the other:
   //   A0 | A1 + V0 | B0 + V1 | B1
-  auto tile = [&](auto st, int t) {
+  // kMask: the tile may hold query rows past L or this block keys past Lk.
+  // Full tiles of a block whose keys are all valid skip the per-element mask.
+  auto tile = [&](auto st, auto masked, int t) {
+    constexpr bool kMask = decltype(masked)::value;
     const unsigned char* qt = qbuf(st);
     const unsigned char* gt = gbuf(st);
     const float* lt = lbuf(st);
     const float* dtv = dbuf(st);
-    f32x16 s0 = zero16, d0 = zero16, s1 = zero16, d1 = zero16;
+    f32x16 s0, d0, s1, d1;
     f32x4 l4[2][4], d4[2][4];
     // rows of register v of unit u: query 32u + 8(v/4) + 4hh + v%4 of the tile
     auto stats = [&](int u) __attribute__((always_inline)) {
@@ -298,25 +301,31 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
       }
     };
     auto grad = [&](f32x16& sv, f32x16& dv_, int u, int v) __attribute__((always_inline)) {
-      const int r = 32 * u + 8 * (v >> 2) + 4 * hh + (v & 3);
-      const bool ok = key_ok && (t * TR + r < L);
-      const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(sv[v], c2, -l4[u][v >> 2][v & 3])) : 0.f;
-      sv[v] = pv;
-      dv_[v] = ok ? pv * (dv_[v] - d4[u][v >> 2][v & 3]) : 0.f;
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sv[v], c2, -l4[u][v >> 2][v & 3]));
+      const float dsv = pv * (dv_[v] - d4[u][v >> 2][v & 3]);
+      if constexpr (kMask) {
+        const int r = 32 * u + 8 * (v >> 2) + 4 * hh + (v & 3);
+        const bool ok = key_ok && (t * TR + r < L);
+        sv[v] = ok ? pv : 0.f;
+        dv_[v] = ok ? dsv : 0.f;
+      } else {
+        sv[v] = pv;
+        dv_[v] = dsv;
+      }
     };
-    // A0
+    // A0 (the first MFMA of each chain takes a zero accumulator)
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 0), kf[kc], s0, 0, 0, 0);
-      d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 0), vf[kc], d0, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 0), kf[kc], kc ? s0 : zero16, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 0), vf[kc], kc ? d0 : zero16, 0, 0, 0);
     }
     stats(0);
     // A1 + V0
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       __builtin_amdgcn_sched_barrier(0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 32), kf[kc], s1, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 32), vf[kc], d1, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 32), kf[kc], kc ? s1 : zero16, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 32), vf[kc], kc ? d1 : zero16, 0, 0, 0);
       grad(s0, d0, 0, 2 * kc);
       grad(s0, d0, 0, 2 * kc + 1);
     }
@@ -346,19 +355,33 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     }
   };
 
+  using Unmasked = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  // pairs of full tiles without masks while the block's keys are all valid,
+  // then the rest (a full tile, the partial last one, or all tiles of a block
+  // that holds padded keys) with masks
+  const int n_unmasked = (kb + 1) * KV_KEYS <= Lk ? L / TR : 0;
   if (nq > 0) load(I0{}, 0);
   int t = 0;
+  for (; t + 2 <= n_unmasked; t += 2) {
+    barrier_loads_done();
+    load(I1{}, t + 1);
+    tile(I0{}, Unmasked{}, t);
+    barrier_loads_done();
+    if (t + 2 < nq) load(I0{}, t + 2);
+    tile(I1{}, Unmasked{}, t + 1);
+  }
   for (; t + 2 <= nq; t += 2) {
     barrier_loads_done();
     load(I1{}, t + 1);
-    tile(I0{}, t);
+    tile(I0{}, Masked{}, t);
     barrier_loads_done();
     if (t + 2 < nq) load(I0{}, t + 2);
-    tile(I1{}, t + 1);
+    tile(I1{}, Masked{}, t + 1);
   }
   if (t < nq) {
     barrier_loads_done();
-    tile(I0{}, t);
+    tile(I0{}, Masked{}, t);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
