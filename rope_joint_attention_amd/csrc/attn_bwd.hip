@@ -313,46 +313,63 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
         dv_[v] = dsv;
       }
     };
-    // A0 (the first MFMA of each chain takes a zero accumulator)
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 0), kf[kc], kc ? s0 : zero16, 0, 0, 0);
-      d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 0), vf[kc], kc ? d0 : zero16, 0, 0, 0);
-    }
+    // The tile is 32 MFMA pairs: 0..7 S, dP of unit 0 (rows of Q, dO); 8..15
+    // the same for unit 1, with the probabilities and dS of unit 0 computed
+    // under them; 16..23 dV, dK of unit 0 (transposed dO, Q) with unit 1's
+    // softmax under them; 24..31 dV, dK of unit 1.  Each pair's two LDS
+    // operands are read one pair ahead, the row statistics eight pairs ahead.
+    auto ops = [&](int i, bf16x8& a, bf16x8& b) __attribute__((always_inline)) {
+      if (i < 16) {
+        const int kc = i & 7, row0 = 32 * (i >> 3);
+        a = row_operand(qt, roff, kc, row0);
+        b = row_operand(gt, roff, kc, row0);
+      } else {
+        const int u = (i - 16) >> 3, j = (i - 16) & 7;
+        const int mm = j >> 2, dt = j & 3;
+        a = tr_operand(gt, troff, dt, 32 * u + 16 * mm);
+        b = tr_operand(qt, troff, dt, 32 * u + 16 * mm);
+      }
+    };
+    bf16x8 ca, cb, na, nb, pb0[2], db0[2], pb1[2], db1[2];
+    ops(0, ca, cb);
     stats(0);
-    // A1 + V0
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
+    for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(qt, roff, kc, 32), kf[kc], kc ? s1 : zero16, 0, 0, 0);
-      d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(gt, roff, kc, 32), vf[kc], kc ? d1 : zero16, 0, 0, 0);
-      grad(s0, d0, 0, 2 * kc);
-      grad(s0, d0, 0, 2 * kc + 1);
+      if (i + 1 < 32) ops(i + 1, na, nb);
+      if (i == 8) stats(1);
+      if (i == 16) {
+        pb0[0] = pack8(s0, 0); pb0[1] = pack8(s0, 8);
+        db0[0] = pack8(d0, 0); db0[1] = pack8(d0, 8);
+      }
+      if (i == 24) {
+        pb1[0] = pack8(s1, 0); pb1[1] = pack8(s1, 8);
+        db1[0] = pack8(d1, 0); db1[1] = pack8(d1, 8);
+      }
+      if (i < 8) {  // the first MFMA of each chain takes a zero accumulator
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[i], i ? s0 : zero16, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, vf[i], i ? d0 : zero16, 0, 0, 0);
+      } else if (i < 16) {
+        const int kc = i - 8;
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[kc], kc ? s1 : zero16, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, vf[kc], kc ? d1 : zero16, 0, 0, 0);
+        grad(s0, d0, 0, 2 * kc);
+        grad(s0, d0, 0, 2 * kc + 1);
+      } else if (i < 24) {
+        const int j = i - 16, mm = j >> 2, dt = j & 3;
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, pb0[mm], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, db0[mm], dk[dt], 0, 0, 0);
+        grad(s1, d1, 1, 2 * j);
+        grad(s1, d1, 1, 2 * j + 1);
+      } else {
+        const int j = i - 24, mm = j >> 2, dt = j & 3;
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, pb1[mm], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, db1[mm], dk[dt], 0, 0, 0);
+      }
+      ca = na;
+      cb = nb;
     }
     __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 pb0[2] = {pack8(s0, 0), pack8(s0, 8)};
-    const bf16x8 db0[2] = {pack8(d0, 0), pack8(d0, 8)};
-    stats(1);
-    // B0 + V1
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int mm = j >> 2, dt = j & 3;
-      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(gt, troff, dt, 16 * mm), pb0[mm], dv[dt], 0, 0, 0);
-      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, troff, dt, 16 * mm), db0[mm], dk[dt], 0, 0, 0);
-      grad(s1, d1, 1, 2 * j);
-      grad(s1, d1, 1, 2 * j + 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 pb1[2] = {pack8(s1, 0), pack8(s1, 8)};
-    const bf16x8 db1[2] = {pack8(d1, 0), pack8(d1, 8)};
-    // B1
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int mm = j >> 2, dt = j & 3;
-      dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(gt, troff, dt, 32 + 16 * mm), pb1[mm], dv[dt], 0, 0, 0);
-      dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, troff, dt, 32 + 16 * mm), db1[mm], dk[dt], 0, 0, 0);
-    }
   };
 
   using Unmasked = std::integral_constant<bool, false>;
@@ -470,7 +487,9 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
     stage_tile(p.v + kbase, sl, t * TR, Lk - 1, vbuf(st), per_wave * wave, per_wave, lane);
   };
 
-  auto tile = [&](auto st, int t) {
+  // kMask: the tile holds keys past Lk (only the last one can)
+  auto tile = [&](auto st, auto masked, int t) {
+    constexpr bool kMask = decltype(masked)::value;
     const unsigned char* kt = kbuf(st);
     const unsigned char* vt = vbuf(st);
     const int lim = Lk - t * TR;
@@ -479,18 +498,22 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
-      f32x16 s = zero16, dp = zero16;
+      f32x16 s, dp;
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, roff, kc, 32 * h), qf[kc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, roff, kc, 32 * h), gf[kc], dp, 0, 0, 0);
+      for (int kc = 0; kc < 8; ++kc) {  // the first MFMA of each chain takes a zero accumulator
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, roff, kc, 32 * h), qf[kc], kc ? s : zero16, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, roff, kc, 32 * h), gf[kc], kc ? dp : zero16, 0, 0, 0);
       }
       // key of register v: 32h + 8(v/4) + 4hh + v%4
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const bool ok = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3) < lim;
-        const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[v], c2, -lse2)) : 0.f;
-        s[v] = ok ? pv * (dp[v] - dlt) : 0.f;  // dS^T
+        const float ds = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -lse2)) * (dp[v] - dlt);  // dS^T
+        if constexpr (kMask) {
+          const bool ok = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3) < lim;
+          s[v] = ok ? ds : 0.f;
+        } else {
+          s[v] = ds;
+        }
       }
       // dQ^T += K^T dS^T, keys in groups of 16
 #pragma unroll
@@ -503,19 +526,31 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
     }
   };
 
+  using Unmasked = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  const int n_full = Lk / TR;  // key tiles with every key valid
   load(I0{}, 0);
   int t = 0;
+  for (; t + 2 <= n_full; t += 2) {
+    barrier_loads_done();
+    load(I1{}, t + 1);
+    tile(I0{}, Unmasked{}, t);
+    barrier_loads_done();
+    if (t + 2 < nk) load(I0{}, t + 2);
+    tile(I1{}, Unmasked{}, t + 1);
+  }
+  // at most one full tile and the partial one remain
   for (; t + 2 <= nk; t += 2) {
     barrier_loads_done();
     load(I1{}, t + 1);
-    tile(I0{}, t);
+    tile(I0{}, Masked{}, t);
     barrier_loads_done();
     if (t + 2 < nk) load(I0{}, t + 2);
-    tile(I1{}, t + 1);
+    tile(I1{}, Masked{}, t + 1);
   }
   if (t < nk) {
     barrier_loads_done();
-    tile(I0{}, t);
+    tile(I0{}, Masked{}, t);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
