@@ -205,10 +205,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // wave index as a scalar: the LDS destinations of the tile loads (M0) are
   // then computed on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Waves w and w+4 share a SIMD.  Fixed, unequal priorities let one of the
-  // pair issue first whenever both are ready, so the other fills its stalls
-  // instead of the two advancing in lockstep (measured: about 0.5 % faster).
-  if (wave < 4) __builtin_amdgcn_s_setprio(2);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
