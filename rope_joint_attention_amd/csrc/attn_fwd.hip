@@ -39,18 +39,19 @@
 //       channel-major tile by tile (v_pack.hip) and each operand is one
 //       16-byte LDS read; without one, V stays in its natural [key][channel]
 //       layout and the operand is gathered with the gfx950 transposing read
-//       ds_read_b64_tr_b16 (two per operand, half the LDS read rate).
+//       ds_read_b64_tr_b16 (two per operand).
 //   The step is software-pipelined: the QK^T MFMAs of tile t+1 run under the
 //   softmax VALU work of tile t, the PV MFMAs of tile t under the row maximum
 //   of tile t+1.
 // LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled within a row (K:
 // slot c ^ (r % 16), V: slot c ^ 4(r % 4)) so that both the K operand reads
-// and the transposing V reads run without bank conflicts.  A packed V tile has
-// 128 rows of 128 bytes (one per channel) with slot c ^ ((r / 2) % 8).  The padded-key
-// mask is a loop bound plus a predicate on the last tile.  Rows past the
-// valid keys are never read: their loads are clamped to the last valid row,
-// whose scores are masked to -inf (K) or whose weights are exactly zero (V),
-// so padding contents cannot reach the output.
+// and the transposing V reads run without bank conflicts.  A packed V tile
+// has 128 rows of 128 bytes (one per channel) with slot c ^ ((r / 2) % 8).
+// The padded-key mask is a loop bound plus a predicate on the last tile.  Rows
+// past the valid keys are never read: their loads are clamped to the last
+// valid row, whose scores are masked to -inf (K) or whose weights are exactly
+// zero (V; packed V holds zeros there instead), so padding contents cannot
+// reach the output.
 #include <type_traits>
 
 #include "hv_internal.h"

@@ -4,8 +4,8 @@
 // section 5.2) contracts over keys, and an MFMA operand wants the contracted
 // index contiguous in each lane: 8 keys of one channel.  V arrives token-major
 // ([token][head][channel]), so without this pass every operand is gathered with
-// the transposing LDS read, which runs at half the rate of a plain 16-byte
-// read.  This kernel rewrites V once per call, tile by tile, channel-major
+// two transposing LDS reads instead of one plain 16-byte read.  This kernel
+// rewrites V once per call, tile by tile, channel-major
 // (layout in hv_internal.h); the attention then streams 16 KB blocks into LDS
 // and reads each operand with one ds_read_b128.  The pass moves 2 x |V| bytes
 // through HBM, about 0.2 % of the attention's time at the largest sizes.
