@@ -130,20 +130,6 @@ __device__ __forceinline__ void barrier_after(void) {
   asm volatile("" ::: "memory");
 }
 
-// ---- scheduling hints -------------------------------------------------------
-constexpr int kSchedVALU = 0x002;
-constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedVMEMRead = 0x020;
-constexpr int kSchedDSRead = 0x100;
-#ifndef HV_ATTN_SCHED
-#define HV_ATTN_SCHED 1
-#endif
-#if HV_ATTN_SCHED
-#define HV_SCHED_GROUP(mask, n, id) __builtin_amdgcn_sched_group_barrier(mask, n, id)
-#else
-#define HV_SCHED_GROUP(mask, n, id) ((void)0)
-#endif
-
 // Row maximum of a score tile (32 in-lane values, then across the two halves),
 // in the log2 domain.  Masked keys must already be -inf.
 __device__ __forceinline__ float tile_max(const f32x16& s0, const f32x16& s1, float c2) {
