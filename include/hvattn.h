@@ -146,10 +146,14 @@ int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
  * call first rewrites V, tile by tile, channel-major into it (one pass over V,
  * 2 x |V| bytes of HBM traffic) and the attention then reads every P V operand
  * with a plain 16-byte LDS read; with workspace == NULL it gathers them from V
- * in place with the transposing LDS read, about 6 % slower at the largest
- * sizes.  Both give bitwise identical results.  A call needs, over its
- * segments with query rows (a batch entry of the padded forms, a packed
- * clip), sum ceil(keys / 64) * 64 * 24 * 128 * 2 bytes;
+ * in place with the transposing LDS read.  The workspace also holds a work
+ * counter through which the attention's workgroups (one per CU) share the
+ * query blocks, so CUs of faster-clocked XCDs take more of them; without it
+ * every XCD gets a fixed share.  The NULL path is about 3 % slower at the
+ * largest sizes; both give bitwise identical results.  A call
+ * needs, over its segments with query rows (a batch entry of the padded
+ * forms, a packed clip), sum ceil(keys / 64) * 64 * 24 * 128 * 2 bytes plus
+ * 256 bytes (none when no segment has query rows);
  * hv_attention_workspace_bytes(n_keys, n_segments) returns an upper bound
  * for n_keys keys in all over n_segments segments:
  *   hv_joint_attention_fwd         n_keys = batch * seq_len, n_segments = batch

@@ -15,15 +15,18 @@
 // merged exactly.
 //
 // Work decomposition
-//   * one workgroup = (segment, head, 256 query rows); 8 waves of 32 rows,
-//     two waves per SIMD;
+//   * one query block = (segment, head, 256 query rows); 8 waves of 32 rows,
+//     two waves per SIMD, one workgroup per CU.  With a workspace the
+//     workgroups are persistent (one per CU) and take query blocks from a
+//     counter; without one each workgroup does one block;
 //   * K and V tiles of 64 keys reach LDS by direct global->LDS loads
 //     (global_load_lds_dwordx4: no registers, fully coalesced 1 KB per wave
 //     instruction) into four LDS stages each for K and V; K tile t+4 and
 //     V tile t+3 are requested during step t, and each wave waits only for
 //     its own oldest loads (s_waitcnt vmcnt) before the step's one barrier;
-//   * workgroup ids are remapped so that consecutive query blocks of one
-//     (batch, head) run on the same XCD and share its L2 for K/V.
+//   * one block per workgroup: workgroup ids are remapped so that
+//     consecutive query blocks of one (batch, head) run on the same XCD and
+//     share its L2 for K/V.
 //
 // Per wave and step, in MFMA 32x32x16 bf16 (fp32 accumulate):
 //   S^T (64 keys x 32 queries) = K_tile * Q^T   -- lane l owns query l%32, so
@@ -196,14 +199,34 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-  // contiguous range of (segment, head, query-block) ids so that the query
-  // blocks resident on one XCD stream the same K/V through its L2.
   const int nb = p.n_blocks;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int per = nb >> 3, extra = nb & 7;
-  const int logical = xcd * per + min(xcd, extra) + (bid >> 3);
+  __shared__ int s_block;
+  for (int iter = 0;; ++iter) {
+  int logical;
+  if constexpr (kPackedV) {
+    // Persistent workgroups, one per CU, take query blocks in order from a
+    // counter in the workspace (zeroed by the packing kernel).  Under MFMA
+    // load the eight XCDs settle at different clocks (measured 1.68-1.85 GHz
+    // on one part); with a fixed share of blocks per XCD the slowest one sets
+    // the time, with the counter the faster ones take more blocks.  Blocks are
+    // numbered segment by segment, head by head, so the 256 blocks in flight
+    // share one head's K/V.
+    __syncthreads();  // the previous block is done with LDS and s_block
+    if (tid == 0) s_block = atomicAdd(p.counter, 1);
+    __syncthreads();
+    logical = __builtin_amdgcn_readfirstlane(s_block);
+    if (logical >= nb) break;
+  } else {
+    // One block per workgroup.  Workgroups are dealt round-robin to the 8
+    // XCDs; give each XCD a contiguous range of (segment, head, query-block)
+    // ids so that the query blocks resident on one XCD stream the same K/V
+    // through its L2.
+    if (iter) break;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    const int per = nb >> 3, extra = nb & 7;
+    logical = xcd * per + min(xcd, extra) + (bid >> 3);
+  }
   int si = 0;  // segment of this block (uniform scan over at most 64 entries)
   for (int i = 1; i < p.n_seg; ++i)
     if (logical >= p.seg[i].blk_begin) si = i;
@@ -547,6 +570,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       p.lse[sg.lse_off + (int64_t)head * p.lse_hstride + orow] =
           (m_run + __log2f(l_tot)) * 0.69314718055994531f;
   }
+  }  // block loop
 }
 
 }  // namespace
@@ -557,6 +581,7 @@ hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream) {
   VtParams vp;
   vp.v = p.v;
   vp.vt = p.vt;
+  vp.counter = nullptr;
   vp.kv_sl = p.kv_sl;
   vp.n_seg = p.n_seg;
   vp.n_blocks = 0;
@@ -581,9 +606,17 @@ hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream) {
   p.n_blocks = blocks;
   if (blocks == 0) return hipSuccess;
   if (p.vt != nullptr) {
+    // the work counter follows the packed tiles
+    p.counter = vp.counter = reinterpret_cast<int*>(p.vt + vt_elems);
     const hipError_t e = launch_v_pack(vp, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+    // one persistent workgroup per CU (128 KB of LDS: one fits per CU)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipGetLastError();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)min(blocks, cus)), dim3(NT), 0, stream, p);
   } else {
     hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
   }

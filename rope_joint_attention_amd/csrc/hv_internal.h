@@ -79,6 +79,7 @@ struct AttnSegment {
 // Packed V (optional workspace): for every segment with query rows, head h
 // and 64-key tile t, a contiguous 16 KB block at
 //   vt + vt_off + (h * ntiles + t) * 8192 elements,  ntiles = ceil(k_len / 64),
+// followed by 256 bytes that hold the attention's work counter,
 // holding the tile channel-major: row d (0..127) is 64 bf16, position p of
 // the row is key 64t + kv_key_of_pos(p) of channel d; keys >= k_len are 0.
 // Inside each group of 16 keys the positions swap bits 2 and 3 of the key
@@ -97,6 +98,7 @@ struct AttnParams {
   uint16_t* out;
   float* lse;          // natural-log log-sum-exp per (head, row); may be null
   uint16_t* vt;        // packed V workspace; null: V is read in place
+  int* counter;        // next query block of the persistent workgroups (packed path)
   int64_t q_sl;        // token strides, elements
   int64_t kv_sl;
   int64_t o_sl;
@@ -108,13 +110,14 @@ struct AttnParams {
   AttnSegment seg[kMaxSegments];
 };
 
-// Bytes of packed V that the segments of p need (segments without query rows
-// need none).
+// Workspace bytes that the segments of p need: packed V (segments without
+// query rows need none) and the 256-byte work counter.
+constexpr int64_t kCounterBytes = 256;
 inline int64_t attn_workspace_bytes(const AttnParams& p) {
   int64_t tiles = 0;
   for (int i = 0; i < p.n_seg; ++i)
     if (p.seg[i].q_len > 0) tiles += (p.seg[i].k_len + 63) / 64;
-  return tiles * HV_HEADS * kVtTileElems * 2;
+  return tiles > 0 ? tiles * HV_HEADS * kVtTileElems * 2 + kCounterBytes : 0;
 }
 
 // Fills blk_begin / nqb / n_blocks from q_len (and vt_off when p.vt is set),
@@ -134,6 +137,7 @@ struct VtSegment {
 struct VtParams {
   const uint16_t* v;
   uint16_t* vt;
+  int* counter;        // the attention's work counter: set to zero here
   int64_t kv_sl;       // token stride of v, elements
   int32_t n_seg;
   int32_t n_blocks;

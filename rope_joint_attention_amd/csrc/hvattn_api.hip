@@ -176,7 +176,7 @@ int hv_version(void) { return 10100; }
 int64_t hv_attention_workspace_bytes(int64_t n_keys, int32_t n_segments) {
   if (n_keys < 0 || n_segments < 0) return 0;
   const int64_t tiles = (n_keys + 63 * (int64_t)n_segments) / 64;
-  return tiles * HV_HEADS * hv::kVtTileElems * 2;
+  return tiles > 0 ? tiles * HV_HEADS * hv::kVtTileElems * 2 + hv::kCounterBytes : 0;
 }
 
 const char* hv_status_string(int status) {

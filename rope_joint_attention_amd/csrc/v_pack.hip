@@ -19,6 +19,9 @@
 //      32-bit LDS reads give the pair for 8 keys, which split into one 16-byte
 //      row piece for each of the two channels.  Eight consecutive lanes write
 //      one whole 128-byte row.
+// Block 0 also zeroes the attention's work counter, which follows the packed
+// tiles in the workspace (a kernel write, so no memset node is recorded when
+// the caller captures the calls in a graph).
 #include "hv_internal.h"
 
 namespace hv {
@@ -46,6 +49,8 @@ __global__ __launch_bounds__(kThreads) void v_pack_kernel(VtParams p) {
   const int head = rel / sg.ntiles;
   const int t = rel - head * sg.ntiles;
   const int tid = threadIdx.x;
+  // the attention that follows on the stream hands out query blocks from here
+  if (blockIdx.x == 0 && tid == 0) *p.counter = 0;
 
   // 1. key row r, channel pairs 16 q4 .. 16 q4 + 15 (four 16-byte chunks)
   {

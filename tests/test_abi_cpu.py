@@ -421,6 +421,7 @@ def test_varlen_bwd_empty_segments_launch_nothing():
 # ------------------------------------------------- packed-V workspace (forward)
 WS = FAKE + 20 * SEP
 TILE_BYTES = 24 * 64 * 128 * 2      # one 64-key tile of packed V for all heads
+COUNTER = 256                        # the attention's work counter after the packed V
 
 
 @pytest.mark.parametrize("n_keys,n_seg,tiles", [
@@ -428,7 +429,7 @@ TILE_BYTES = 24 * 64 * 128 * 2      # one 64-key tile of packed V for all heads
     (2 * 300, 2, 11), (100, 3, 4), (-1, 1, 0), (5, -1, 0),   # floor((n + 63 s) / 64) tiles
 ])
 def test_workspace_bytes(n_keys, n_seg, tiles):
-    assert hv.hv_attention_workspace_bytes(n_keys, n_seg) == tiles * TILE_BYTES
+    assert hv.hv_attention_workspace_bytes(n_keys, n_seg) == (tiles * TILE_BYTES + COUNTER if tiles else 0)
 
 
 def test_workspace_bound_covers_every_split():
@@ -437,14 +438,15 @@ def test_workspace_bound_covers_every_split():
     r = random.Random(5)
     for _ in range(2000):
         ks = [r.randint(0, 300) for _ in range(r.randint(1, 64))]
-        need = sum((k + 63) // 64 for k in ks) * TILE_BYTES
+        tiles = sum((k + 63) // 64 for k in ks)
+        need = tiles * TILE_BYTES + COUNTER if tiles else 0
         assert need <= hv.hv_attention_workspace_bytes(sum(ks), len(ks))
 
 
 # default attn(): one segment of 40 + 10 keys = 1 tile; attn_lse(): 300 keys = 5
 # tiles; varlen(): segments of 100 and 200 keys = 2 + 4 tiles
-@pytest.mark.parametrize("call,need", [(attn, TILE_BYTES), (attn_lse, 5 * TILE_BYTES),
-                                       (varlen, 6 * TILE_BYTES)])
+@pytest.mark.parametrize("call,need", [(attn, TILE_BYTES + COUNTER), (attn_lse, 5 * TILE_BYTES + COUNTER),
+                                       (varlen, 6 * TILE_BYTES + COUNTER)])
 def test_workspace_validation(call, need):
     assert call(ws=WS, ws_bytes=need - 1) == E                  # too small
     assert call(ws=WS, ws_bytes=0) == E
@@ -458,7 +460,7 @@ def test_workspace_validation(call, need):
 
 
 def test_workspace_must_not_meet_lse():
-    need = 6 * TILE_BYTES
-    assert attn_lse(ws=LSE - 128, ws_bytes=5 * TILE_BYTES) == E
+    need = 6 * TILE_BYTES + COUNTER
+    assert attn_lse(ws=LSE - 128, ws_bytes=5 * TILE_BYTES + COUNTER) == E
     assert varlen(ws=LSE + 256, ws_bytes=need) == E
 

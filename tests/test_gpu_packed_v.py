@@ -12,8 +12,10 @@ same MFMA slots, so the outputs (and log-sum-exps) must agree bit for bit.
   packed segments with empty ones in between;
 * the workspace holds exactly the documented packed layout (per segment,
   head and tile: 128 channel rows of 64 keys, keys swapped in bits 2 and 3
-  inside each group of 16, zeros past the valid keys) and nothing past the
-  bytes the call needs is written;
+  inside each group of 16, zeros past the valid keys), then the work counter
+  through which the persistent workgroups took the query blocks (it ends at
+  blocks + workgroups: every workgroup's last take finds no block), and
+  nothing past the bytes the call needs is written;
 * one workspace reused by two calls in a row, the second smaller; poisoned
   padded rows never reach the workspace; a too-small workspace is refused.
 Parity with the fp64 oracle for the packed path is covered by every other GPU
@@ -126,7 +128,7 @@ def test_workspace_holds_the_packed_layout():
     vb = bits["v"].copy()
     vb[1, n_video + 7:] = 0x7FC0                     # NaN in the padded rows of entry 1
     q, k, v = bits_to_torch(bits["q"]), bits_to_torch(bits["k"]), bits_to_torch(vb)
-    need = sum((n_video + x + 63) // 64 for x in valid) * 24 * TILE * 2
+    need = sum((n_video + x + 63) // 64 for x in valid) * 24 * TILE * 2 + 256
     cap_bytes = hv.hv_attention_workspace_bytes(B * L, B)
     assert cap_bytes >= need
     ws = torch.full((cap_bytes // 2,), 0x1234, dtype=torch.int16, device="cuda")
@@ -135,9 +137,13 @@ def test_workspace_holds_the_packed_layout():
     torch.cuda.synchronize()
     got = ws.cpu().numpy().view(np.uint16)
     want = np.concatenate([expected_packed(vb[b], [n_video + valid[b]], [0]) for b in range(B)])
-    assert want.size * 2 == need
+    assert want.size * 2 + 256 == need
     assert np.array_equal(got[:want.size], want)
-    assert (got[want.size:] == 0x1234).all()          # nothing past what the call needs
+    blocks = B * 24 * ((L + 255) // 256)
+    groups = min(blocks, torch.cuda.get_device_properties(0).multi_processor_count)
+    counter = int(got[want.size:want.size + 2].view(np.int32)[0])
+    assert counter == blocks + groups
+    assert (got[want.size + 2:] == 0x1234).all()      # nothing else past the packed tiles
     o = widen(torch_to_bits(out))
     assert np.isfinite(o).all()
     ref = joint_attention(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), n_video, valid)
