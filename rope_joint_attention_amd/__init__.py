@@ -304,6 +304,25 @@ def _lse_buffer(lse, shape, device, what: str):
     return lse
 
 
+BWD_COUNTER_FLOATS = 64   # the 256 bytes of work counters after D in the backward's workspace
+
+
+def _delta_workspace(delta, n_rows: int, device):
+    """The backward's delta workspace: n_rows * 24 floats of D, then the
+    counters.  A given tensor must be a contiguous float32 tensor with at least
+    that many elements."""
+    import torch
+
+    need = n_rows * HV_HEADS + BWD_COUNTER_FLOATS
+    if delta is None:
+        return torch.empty(need, dtype=torch.float32, device=device)
+    if delta.dtype != torch.float32 or delta.device != device or not delta.is_contiguous() \
+            or delta.numel() < need:
+        raise ValueError(f"delta must be a contiguous float32 tensor of at least {need} elements "
+                         f"(24 per row, then {BWD_COUNTER_FLOATS} for the work counters)")
+    return delta
+
+
 def hv_attention_fwd_lse(q, k, v, kv_valid_len: Optional[Sequence[int]] = None, out=None,
                          lse=None, want_lse: bool = True, softmax_scale: Optional[float] = None,
                          workspace=None, pack_v: bool = True):
@@ -435,7 +454,7 @@ def hv_joint_attention_bwd(q, k, v, out, dout, lse, text_valid_len: Optional[Seq
             raise ValueError(f"q and {name} must share shape and strides")
     shape = (q.shape[0], HV_HEADS, q.shape[1])
     _lse_buffer(lse, shape, q.device, "lse")
-    delta = _lse_buffer(delta, shape, q.device, "delta")
+    delta = _delta_workspace(delta, q.shape[0] * q.shape[1], q.device)
     grads = []
     for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if g is None:
@@ -480,7 +499,7 @@ def hv_joint_attention_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q: Sequenc
             raise ValueError(f"q and {name} must share shape and strides")
     shape = (HV_HEADS, q.shape[0])
     _lse_buffer(lse, shape, q.device, "lse")
-    delta = _lse_buffer(delta, shape, q.device, "delta")
+    delta = _delta_workspace(delta, q.shape[0], q.device)
     grads = []
     for g, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
         if g is None:

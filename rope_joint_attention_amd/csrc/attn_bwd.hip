@@ -132,13 +132,17 @@ __device__ __forceinline__ bf16x8 row_operand(const unsigned char* tile, const i
   return *reinterpret_cast<const bf16x8*>(tile + off[kc] + row0 * ROWB);
 }
 
-// XCD-aware block order (workgroups are dealt round-robin to the 8 XCDs):
-// consecutive logical ids, which share a (batch, head), land on one XCD.
-__device__ __forceinline__ int logical_block(int nb) {
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int per = nb >> 3, extra = nb & 7;
-  return xcd * per + min(xcd, extra) + (bid >> 3);
+// Persistent workgroups, one per CU, take blocks in order from a counter
+// (zeroed by the delta kernel that runs first): under MFMA load the XCDs settle
+// at different clocks, and a fixed share of blocks per XCD would let the
+// slowest one set the time.  Returns the next block, or a value >= nb when
+// the work is done.  The first barrier makes sure every wave is done with the
+// previous block's LDS before the caller stages new tiles.
+__device__ __forceinline__ int next_block(int* counter, int& slot) {
+  __syncthreads();
+  if (threadIdx.x == 0) slot = atomicAdd(counter, 1);
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(slot);
 }
 
 // Stage one 64-row tile (rows row0.. of a [rows][stride] bf16 tensor, last
@@ -175,6 +179,10 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // work counters of the two gradient kernels
+    p.counters[0] = 0;
+    p.counters[1] = 0;
+  }
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int chunk = (int)(gid & 15);
   const int64_t row = gid >> 4;  // b * seq_len + n
@@ -225,7 +233,10 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int logical = logical_block(p.n_kv_blocks);
+  __shared__ int s_block;
+  for (;;) {
+  const int logical = next_block(p.counters + 0, s_block);
+  if (logical >= p.n_kv_blocks) break;
   int si = 0;  // segment of this block (uniform scan over at most 64 entries)
   for (int i = 1; i < p.n_seg; ++i)
     if (logical >= p.seg[i].k_blk) si = i;
@@ -420,6 +431,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
         *reinterpret_cast<u32x2*>(vp + dt * 32 + 8 * j + 4 * hh) = wv;
       }
   }
+  }  // block loop
 }
 
 // --------------------------------------------------------------------- dQ --
@@ -438,7 +450,10 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
-  const int logical = logical_block(p.n_q_blocks);
+  __shared__ int s_block;
+  for (;;) {
+  const int logical = next_block(p.counters + 1, s_block);
+  if (logical >= p.n_q_blocks) break;
   int si = 0;
   for (int i = 1; i < p.n_seg; ++i)
     if (logical >= p.seg[i].q_blk) si = i;
@@ -568,6 +583,7 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
         *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * j + 4 * hh) = w;
       }
   }
+  }  // block loop
 }
 
 }  // namespace
@@ -586,14 +602,24 @@ hipError_t launch_attn_bwd(BwdParams& p, hipStream_t stream) {
   p.n_q_blocks = qblocks;
   p.n_kv_blocks = kblocks;
   if (qblocks == 0 && kblocks == 0) return hipSuccess;
+  // the two work counters follow D in the caller's workspace
+  p.counters = reinterpret_cast<int*>(p.delta + (int64_t)p.batch * HV_HEADS * p.seq_len);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipGetLastError();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  // D for every row (and the counters' reset): it runs first on the stream
   const int64_t threads = (int64_t)p.batch * p.seq_len * 16;
-  if (threads > 0 && qblocks > 0)  // D is only read when some segment has queries
-    hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, p);
+  hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)std::max<int64_t>(1, (threads + 255) / 256)),
+                     dim3(256), 0, stream, p);
+  // one persistent workgroup per CU (each kernel's LDS or registers allow one)
   if (kblocks > 0)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)kblocks), dim3(KV_WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)std::min(kblocks, cus)), dim3(KV_WAVES * 64), 0,
+                       stream, p);
   if (qblocks > 0)
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)qblocks), dim3(Q_WAVES * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)std::min(qblocks, cus)), dim3(Q_WAVES * 64), 0,
+                       stream, p);
   return hipGetLastError();
 }
 

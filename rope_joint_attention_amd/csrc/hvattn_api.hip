@@ -92,7 +92,8 @@ float scale_log2(float softmax_scale) {
 }
 
 // Pointers, alignment and overlap of the backward's arguments (shared by the
-// padded and the packed forms).  lse and delta hold batch * 24 * seq_len floats.
+// padded and the packed forms).  lse holds batch * 24 * seq_len floats; delta
+// as many, followed by 256 bytes of work counters.
 int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, const hv_bf16* out,
                       const hv_bf16* dout, const float* lse, hv_bf16* dq, hv_bf16* dk, hv_bf16* dv,
                       float* delta, const hv_layout* layout) {
@@ -114,12 +115,13 @@ int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, cons
       if (overlap(outs[i], outs[j], layout, extent)) return HV_ERR_INVALID_ARG;
   }
   const uintptr_t vb = (uintptr_t)layout->batch * HV_HEADS * layout->seq_len * sizeof(float);
+  const uintptr_t db = vb + hv::kCounterBytes;  // D, then the two kernels' work counters
   const uintptr_t tb = (uintptr_t)extent * sizeof(hv_bf16);
-  if (ranges_meet(delta, vb, lse, vb)) return HV_ERR_INVALID_ARG;
+  if (ranges_meet(delta, db, lse, vb)) return HV_ERR_INVALID_ARG;
   for (const hv_bf16* t : ins)
-    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
+    if (ranges_meet(delta, db, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
   for (const hv_bf16* t : outs)
-    if (ranges_meet(delta, vb, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
+    if (ranges_meet(delta, db, t, tb) || ranges_meet(lse, vb, t, tb)) return HV_ERR_INVALID_ARG;
   return HV_OK;
 }
 
@@ -171,7 +173,7 @@ void rope_frequencies(float theta, float* freq) {
 
 extern "C" {
 
-int hv_version(void) { return 10100; }
+int hv_version(void) { return 10200; }
 
 int64_t hv_attention_workspace_bytes(int64_t n_keys, int32_t n_segments) {
   if (n_keys < 0 || n_segments < 0) return 0;

@@ -383,6 +383,19 @@ def test_backward_validation(kwargs, expect):
     assert bwd(**kwargs) == expect
 
 
+D_BYTES = 24 * 300 * 4       # D of the default layout; 256 bytes of work counters follow it
+
+
+def test_backward_delta_includes_the_counters():
+    # (arguments that pass every check would launch on these fake pointers,
+    # so only refusals are asked for here)
+    assert bwd(delta=LSE - D_BYTES) == E                  # counters would overwrite lse
+    assert bwd(delta=LSE - D_BYTES - 252) == E
+    assert bwd(lse=FAKE + 13 * SEP + D_BYTES + 128) == E
+    assert bwd(dq=FAKE + 13 * SEP + D_BYTES + 240, dk=FAKE + 11 * SEP) == E
+    assert varlen_bwd(delta=LSE - D_BYTES) == E
+
+
 def test_backward_empty_call():
     assert bwd(lay=layout(batch=0), valid=None, n_video=0) == hv.HV_OK
 
