@@ -24,6 +24,8 @@
 //   * dq:    one workgroup per (batch, head, 256 queries), 8 waves of 32
 //            queries (two per SIMD) with Q and dO in registers; it walks the key tiles of 64
 //            rows (K, V staged the same way) and accumulates dQ^T += K^T dS^T.
+// The dkdv and dq grids are persistent: one workgroup per CU, each taking
+// (batch, head, rows) blocks in order from a work counter until none is left.
 // dQ is computed in its own pass (recomputing S and dP) instead of by atomics
 // from the key-block kernel: no fp32 scratch, deterministic results.
 //
