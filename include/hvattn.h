@@ -276,7 +276,7 @@ int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_b
  *   delta               device workspace of batch * 24 * seq_len floats plus
  *                       256 bytes (caller-owned, 4-byte aligned, disjoint from
  *                       all other arguments): the first part receives
- *                       rowsum(dO * O) as fp32 [batch][24][seq_len]; the last
+ *                       -rowsum(dO * O) as fp32 [batch][24][seq_len]; the last
  *                       256 bytes hold the work counters through which the
  *                       two gradient kernels' persistent workgroups (one per
  *                       CU) take their blocks.  Its contents need no

@@ -13,7 +13,10 @@
 // so no running maximum is needed.  Padded keys get zero dK, dV.
 //
 // Three kernels, all MFMA 32x32x16 bf16 with fp32 accumulation:
-//   * delta: D per (row, head), one thread per 16-byte chunk, 16-lane DPP sum;
+//   * delta: D per (row, head), one thread per 16-byte chunk, 16-lane DPP sum,
+//            stored negated: -D is where every dP accumulation starts, so the
+//            MFMAs yield dP - D directly (and the dkdv kernel's S chains start
+//            from -lse/scale, so the exponent is one multiply away);
 //   * dkdv:  one workgroup per (batch, head, 128 keys), 4 waves of 32 keys,
 //            K and V of its keys held in registers as MFMA operands; it walks
 //            all query tiles of 64 rows (Q, dO, lse, D staged in LDS by
@@ -211,7 +214,8 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
         s = fmaf(__uint_as_float(ov[i][j] & 0xffff0000u), __uint_as_float(gv[i][j] & 0xffff0000u), s);
       }
       s = row16_sum(s);
-      if (chunk == 0) p.delta[((int64_t)b * HV_HEADS + h0 + i) * p.seq_len + n] = s;
+      // stored negated: it is the starting accumulator of the dP products
+      if (chunk == 0) p.delta[((int64_t)b * HV_HEADS + h0 + i) * p.seq_len + n] = -s;
     }
   }
 }
@@ -276,8 +280,8 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) dk[dt][v] = dv[dt][v] = 0.f;
-  const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float c2 = p.scale_log2;
+  const float nis = -1.0f / p.scale;
   // a block of padded keys only has zero gradients: skip the query loop
   const int nq = kb * KV_KEYS >= Lk || L == 0 ? 0 : (L + TR - 1) / TR;
 
@@ -303,19 +307,27 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     const float* lt = lbuf(st);
     const float* dtv = dbuf(st);
     f32x16 s0, d0, s1, d1;
-    f32x4 l4[2][4], d4[2][4];
-    // rows of register v of unit u: query 32u + 8(v/4) + 4hh + v%4 of the tile
+    // Starting accumulators of unit u, row by row (register v of a unit holds
+    // query 32u + 8(v/4) + 4hh + v%4 of the tile): -lse/scale for S, so that
+    // scale*log2(e) times the result is the log2 of P, and -D for dP, so that
+    // the result is dP - D.
+    f32x16 si[2], di[2];
     auto stats = [&](int u) __attribute__((always_inline)) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r = 32 * u + 8 * g + 4 * hh;
-        l4[u][g] = *reinterpret_cast<const f32x4*>(lt + r) * kLog2e;
-        d4[u][g] = *reinterpret_cast<const f32x4*>(dtv + r);
+        const f32x4 l = *reinterpret_cast<const f32x4*>(lt + r) * nis;
+        const f32x4 d = *reinterpret_cast<const f32x4*>(dtv + r);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          si[u][4 * g + j] = l[j];
+          di[u][4 * g + j] = d[j];
+        }
       }
     };
     auto grad = [&](f32x16& sv, f32x16& dv_, int u, int v) __attribute__((always_inline)) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(sv[v], c2, -l4[u][v >> 2][v & 3]));
-      const float dsv = pv * (dv_[v] - d4[u][v >> 2][v & 3]);
+      const float pv = __builtin_amdgcn_exp2f(sv[v] * c2);
+      const float dsv = pv * dv_[v];
       if constexpr (kMask) {
         const int r = 32 * u + 8 * (v >> 2) + 4 * hh + (v & 3);
         const bool ok = key_ok && (t * TR + r < L);
@@ -330,7 +342,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     // the same for unit 1, with the probabilities and dS of unit 0 computed
     // under them; 16..23 dV, dK of unit 0 (transposed dO, Q) with unit 1's
     // softmax under them; 24..31 dV, dK of unit 1.  Each pair's two LDS
-    // operands are read one pair ahead, the row statistics eight pairs ahead.
+    // operands are read one pair ahead, the row statistics four pairs ahead.
     auto ops = [&](int i, bf16x8& a, bf16x8& b) __attribute__((always_inline)) {
       if (i < 16) {
         const int kc = i & 7, row0 = 32 * (i >> 3);
@@ -350,7 +362,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       if (i + 1 < 32) ops(i + 1, na, nb);
-      if (i == 8) stats(1);
+      if (i == 4) stats(1);
       if (i == 16) {
         pb0[0] = pack8(s0, 0); pb0[1] = pack8(s0, 8);
         db0[0] = pack8(d0, 0); db0[1] = pack8(d0, 8);
@@ -359,13 +371,13 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
         pb1[0] = pack8(s1, 0); pb1[1] = pack8(s1, 8);
         db1[0] = pack8(d1, 0); db1[1] = pack8(d1, 8);
       }
-      if (i < 8) {  // the first MFMA of each chain takes a zero accumulator
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[i], i ? s0 : zero16, 0, 0, 0);
-        d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, vf[i], i ? d0 : zero16, 0, 0, 0);
+      if (i < 8) {  // the first MFMA of each chain takes the starting accumulator
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[i], i ? s0 : si[0], 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, vf[i], i ? d0 : di[0], 0, 0, 0);
       } else if (i < 16) {
         const int kc = i - 8;
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[kc], kc ? s1 : zero16, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, vf[kc], kc ? d1 : zero16, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[kc], kc ? s1 : si[1], 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, vf[kc], kc ? d1 : di[1], 0, 0, 0);
         grad(s0, d0, 0, 2 * kc);
         grad(s0, d0, 0, 2 * kc + 1);
       } else if (i < 24) {
@@ -483,7 +495,12 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
     }
   }
   const float lse2 = p.lse[vbase + qrow] * kLog2e;
-  const float dlt = p.delta[vbase + qrow];
+  f32x16 neg_d;  // -D of this lane's query (as stored): the dP^T chains start from it
+  {
+    const float nd = p.delta[vbase + qrow];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) neg_d[v] = nd;
+  }
   int roff[8], troff[8];
   row_offsets(l32, hh, roff);
   tr_offsets(lane, troff);
@@ -517,14 +534,14 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
       // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
       f32x16 s, dp;
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {  // the first MFMA of each chain takes a zero accumulator
+      for (int kc = 0; kc < 8; ++kc) {  // S^T starts from zero, dP^T from -D
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(kt, roff, kc, 32 * h), qf[kc], kc ? s : zero16, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, roff, kc, 32 * h), gf[kc], kc ? dp : zero16, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_operand(vt, roff, kc, 32 * h), gf[kc], kc ? dp : neg_d, 0, 0, 0);
       }
       // key of register v: 32h + 8(v/4) + 4hh + v%4
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float ds = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -lse2)) * (dp[v] - dlt);  // dS^T
+        const float ds = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -lse2)) * dp[v];  // dS^T
         if constexpr (kMask) {
           const bool ok = 32 * h + 8 * (v >> 2) + 4 * hh + (v & 3) < lim;
           s[v] = ok ? ds : 0.f;

