@@ -24,9 +24,10 @@
 //     instruction) into four LDS stages each for K and V; K tile t+4 and
 //     V tile t+3 are requested during step t, and each wave waits only for
 //     its own oldest loads (s_waitcnt vmcnt) before the step's one barrier;
-//   * one block per workgroup: workgroup ids are remapped so that
-//     consecutive query blocks of one (batch, head) run on the same XCD and
-//     share its L2 for K/V.
+//   * blocks are numbered segment by segment and head by head, so the blocks
+//     in flight stream the same K/V; without a workspace (one block per
+//     workgroup) workgroup ids are remapped so that consecutive query blocks
+//     of one (batch, head) run on the same XCD and share its L2.
 //
 // Per wave and step, in MFMA 32x32x16 bf16 (fp32 accumulate):
 //   S^T (64 keys x 32 queries) = K_tile * Q^T   -- lane l owns query l%32, so
