@@ -126,10 +126,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // caller waits for exactly the loads and LDS operations that must be
 // complete; the empty asm statements keep the compiler from moving memory
 // accesses across the barrier.
-template <int kVm>
+template <int kVm, int kLgkm = 0>
 __device__ __forceinline__ void barrier_after(void) {
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kVm, 0));
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kVm, kLgkm));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -417,25 +417,34 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   }
   if (ntiles == 1) mask_tile(sa[0], sa[1], Lk, hh);
   update_reference(tile_max(sa[0], sa[1], c2), m_run, l_run, o);
-  // K operands of the first step (tile 1) are read before its barrier
+  // K operands of the first step (tile 1) are read, and its first two QK^T
+  // MFMAs issued, before its barrier (see the end of a step)
   bf16x8 kf[4];
   kf[0] = k_frag(I1{}, 0, 0);
   kf[1] = k_frag(I1{}, 1, 0);
   kf[2] = k_frag(I1{}, 0, 1);
   kf[3] = k_frag(I1{}, 1, 1);
+  sb[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], zero16, 0, 0, 0);
+  sb[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1], qf[0], zero16, 0, 0, 0);
+  kf[0] = k_frag(I1{}, 0, 2);
+  kf[1] = k_frag(I1{}, 1, 2);
   barrier_after<0>();  // every wave has read K tile 0 before its buffer is refilled
 
   // ---- steady state.  Step t (tile t+1 exists; U = t % 4 at compile time),
   // in fixed instruction order (sched_barrier fences between bundles keep the
   // compiler from regrouping):
-  //   phase 1: QK^T MFMAs of tile t+1 (its first K operands were read before
-  //            the previous barrier, the rest two chunks ahead), each followed
-  //            by exp2 / bf16 / sum work for keys 0..31 of tile t;
+  //   phase 1: QK^T MFMAs of tile t+1 (its first chunk was issued before the
+  //            previous barrier, the operands of the next two were read there,
+  //            the rest two chunks ahead), each followed by exp2 / bf16 / sum
+  //            work for keys 0..31 of tile t;
   //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead); the first
   //            eight carry the exp2 work for keys 32..63, the next four the row
   //            maximum of tile t+1;
-  //   then requests for K tile t+4 and V tile t+3, the first K operands of
-  //   tile t+2 for the next step, one barrier and the reference update.
+  //   then the first K operands of tile t+2, requests for K tile t+4 and V
+  //   tile t+3, the first chunk of QK^T MFMAs of tile t+2 (into the score
+  //   registers of tile t, free by then), so that the MFMA pipe has work
+  //   queued while the waves meet at the barrier, and the operands of its
+  //   second and third chunks; one barrier and the reference update.
   // K tile t+1 and V tile t were requested three steps earlier (or in the
   // prologue); every barrier waits for the loads of the step before it, so a
   // tile is complete and visible from the barrier that follows its request
@@ -450,12 +459,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     refresh_offsets();
     bf16x8 pb[4];
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
+    for (int kc = 1; kc < 8; ++kc) {  // chunk 0 was issued before the barrier
       __builtin_amdgcn_sched_barrier(0);
       const int sl0 = 2 * (kc & 1);
-      nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0], qf[kc], kc ? nxt[0] : zero16, 0, 0, 0);
+      nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0], qf[kc], nxt[0], 0, 0, 0);
+      if (kc == 1) exp_pair(cur, 0);
       exp_pair(cur, 2 * kc);  // keys 0..31 of tile t (score registers 0..15 of cur[0])
-      nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0 + 1], qf[kc], kc ? nxt[1] : zero16, 0, 0, 0);
+      nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0 + 1], qf[kc], nxt[1], 0, 0, 0);
       if (kc == 3) pb[0] = pack_p(cur, 0);
       if (kc == 7) pb[1] = pack_p(cur, 1);
       if (kc + 2 < 8) {
@@ -502,7 +512,16 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     load_k(KL{}, min(t + KAHEAD, ntiles - 1));
     load_v(VL{}, min(t + VAHEAD, ntiles - 1));
     const float mx = max_across_halves(part_run) * c2;
-    barrier_after<4>();  // the 4 loads just issued stay in flight
+    __builtin_amdgcn_sched_barrier(0);
+    // chunk 0 of tile t+2 (after the last step: a tile that is never used)
+    cur[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], zero16, 0, 0, 0);
+    cur[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1], qf[0], zero16, 0, 0, 0);
+    kf[0] = k_frag(KN{}, 0, 2);
+    kf[1] = k_frag(KN{}, 1, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // the 4 loads just issued stay in flight, and so may the two reads of K
+    // tile t+2 (its stage is not refilled before the next barrier)
+    barrier_after<4, 2>();
     update_reference(mx, m_run, l_run, o);
   };
 
