@@ -167,6 +167,31 @@ __device__ __forceinline__ void stage_tile(const uint16_t* base, int64_t stride,
   }
 }
 
+// Per-lane byte offsets, from the first row of a full tile, of the `n`
+// staging instructions i0 .. i0+n-1 (the same rows and slots as stage_tile).
+template <int N>
+__device__ __forceinline__ void stage_offsets(int64_t stride, int i0, int lane, uint32_t (&off)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int r = 4 * (i0 + j) + (lane >> 4);
+    const int c = (lane & 15) ^ swz(r & 15);
+    off[j] = (uint32_t)(r * stride * 2) + c * 16;
+  }
+}
+
+// stage_tile for a tile whose 64 rows all exist: a scalar tile address plus
+// the precomputed 32-bit lane offsets, no per-lane address arithmetic.
+template <int N>
+__device__ __forceinline__ void stage_full_tile(const uint16_t* base, int64_t stride, int row0,
+                                                unsigned char* tile, int i0, uint32_t (&off)[N]) {
+  const unsigned char* tb = (const unsigned char*)(base + (int64_t)row0 * stride);
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    asm volatile("" : "+v"(off[j]));  // keeps the scalar base + 32-bit offset form
+    __builtin_amdgcn_global_load_lds(tb + off[j], (HV_LDS void*)(tile + (i0 + j) * 1024), 16, 0, 0);
+  }
+}
+
 // 64 consecutive fp32 values (rows row0.., clamped to `last`) of a row vector.
 __device__ __forceinline__ void stage_vec(const float* base, int row0, int last, float* dst,
                                           int lane) {
@@ -286,9 +311,16 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   const int nq = kb * KV_KEYS >= Lk || L == 0 ? 0 : (L + TR - 1) / TR;
 
   // 16 instructions per 64-row tile and tensor: wave w issues 4w .. 4w+3
+  uint32_t soff[4];
+  stage_offsets(sl, 4 * wave, lane, soff);
   auto load = [&](auto st, int t) {
-    stage_tile(p.q + qbase, sl, t * TR, L - 1, qbuf(st), 4 * wave, 4, lane);
-    stage_tile(p.dout + qbase, sl, t * TR, L - 1, gbuf(st), 4 * wave, 4, lane);
+    if (t * TR + TR <= L) {
+      stage_full_tile(p.q + qbase, sl, t * TR, qbuf(st), 4 * wave, soff);
+      stage_full_tile(p.dout + qbase, sl, t * TR, gbuf(st), 4 * wave, soff);
+    } else {
+      stage_tile(p.q + qbase, sl, t * TR, L - 1, qbuf(st), 4 * wave, 4, lane);
+      stage_tile(p.dout + qbase, sl, t * TR, L - 1, gbuf(st), 4 * wave, 4, lane);
+    }
     if (wave == 0) stage_vec(p.lse + vbase, t * TR, L - 1, lbuf(st), lane);
     if (wave == 1) stage_vec(p.delta + vbase, t * TR, L - 1, dbuf(st), lane);
   };
@@ -325,18 +357,29 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
         }
       }
     };
-    auto grad = [&](f32x16& sv, f32x16& dv_, int u, int v) __attribute__((always_inline)) {
-      const float pv = __builtin_amdgcn_exp2f(sv[v] * c2);
-      const float dsv = pv * dv_[v];
+    // P and dS of scores 2w, 2w+1 of unit u, rounded to bf16 straight into
+    // word w of the unit's dV and dK operands (the accumulators are only read)
+    uint32_t pw[2][8], dw[2][8];
+    auto grad = [&](const f32x16& sv, const f32x16& dv_, int u, int w) __attribute__((always_inline)) {
+      float p0 = __builtin_amdgcn_exp2f(sv[2 * w] * c2);
+      float p1 = __builtin_amdgcn_exp2f(sv[2 * w + 1] * c2);
+      float g0 = p0 * dv_[2 * w];
+      float g1 = p1 * dv_[2 * w + 1];
       if constexpr (kMask) {
-        const int r = 32 * u + 8 * (v >> 2) + 4 * hh + (v & 3);
-        const bool ok = key_ok && (t * TR + r < L);
-        sv[v] = ok ? pv : 0.f;
-        dv_[v] = ok ? dsv : 0.f;
-      } else {
-        sv[v] = pv;
-        dv_[v] = dsv;
+        const int r = 32 * u + 8 * (w >> 1) + 4 * hh + 2 * (w & 1);  // rows r, r + 1
+        const bool ok0 = key_ok && (t * TR + r < L);
+        const bool ok1 = key_ok && (t * TR + r + 1 < L);
+        p0 = ok0 ? p0 : 0.f;
+        g0 = ok0 ? g0 : 0.f;
+        p1 = ok1 ? p1 : 0.f;
+        g1 = ok1 ? g1 : 0.f;
       }
+      pw[u][w] = pack_bf16(p0, p1);
+      dw[u][w] = pack_bf16(g0, g1);
+    };
+    auto words = [&](const uint32_t (&wd)[8], int h) __attribute__((always_inline)) {
+      const u32x4 v = {wd[4 * h], wd[4 * h + 1], wd[4 * h + 2], wd[4 * h + 3]};
+      return __builtin_bit_cast(bf16x8, v);
     };
     // The tile is 32 MFMA pairs: 0..7 S, dP of unit 0 (rows of Q, dO); 8..15
     // the same for unit 1, with the probabilities and dS of unit 0 computed
@@ -364,12 +407,12 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
       if (i + 1 < 32) ops(i + 1, na, nb);
       if (i == 4) stats(1);
       if (i == 16) {
-        pb0[0] = pack8(s0, 0); pb0[1] = pack8(s0, 8);
-        db0[0] = pack8(d0, 0); db0[1] = pack8(d0, 8);
+        pb0[0] = words(pw[0], 0); pb0[1] = words(pw[0], 1);
+        db0[0] = words(dw[0], 0); db0[1] = words(dw[0], 1);
       }
       if (i == 24) {
-        pb1[0] = pack8(s1, 0); pb1[1] = pack8(s1, 8);
-        db1[0] = pack8(d1, 0); db1[1] = pack8(d1, 8);
+        pb1[0] = words(pw[1], 0); pb1[1] = words(pw[1], 1);
+        db1[0] = words(dw[1], 0); db1[1] = words(dw[1], 1);
       }
       if (i < 8) {  // the first MFMA of each chain takes the starting accumulator
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[i], i ? s0 : si[0], 0, 0, 0);
@@ -378,14 +421,12 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
         const int kc = i - 8;
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, kf[kc], kc ? s1 : si[1], 0, 0, 0);
         d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, vf[kc], kc ? d1 : di[1], 0, 0, 0);
-        grad(s0, d0, 0, 2 * kc);
-        grad(s0, d0, 0, 2 * kc + 1);
+        grad(s0, d0, 0, kc);
       } else if (i < 24) {
         const int j = i - 16, mm = j >> 2, dt = j & 3;
         dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, pb0[mm], dv[dt], 0, 0, 0);
         dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, db0[mm], dk[dt], 0, 0, 0);
-        grad(s1, d1, 1, 2 * j);
-        grad(s1, d1, 1, 2 * j + 1);
+        grad(s1, d1, 1, j);
       } else {
         const int j = i - 24, mm = j >> 2, dt = j & 3;
         dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca, pb1[mm], dv[dt], 0, 0, 0);
@@ -516,9 +557,16 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
 
   // 16 instructions per tile and tensor, split evenly over the waves
   constexpr int per_wave = 16 / Q_WAVES;
+  uint32_t soff[per_wave];
+  stage_offsets(sl, per_wave * wave, lane, soff);
   auto load = [&](auto st, int t) {
-    stage_tile(p.k + kbase, sl, t * TR, Lk - 1, kbuf(st), per_wave * wave, per_wave, lane);
-    stage_tile(p.v + kbase, sl, t * TR, Lk - 1, vbuf(st), per_wave * wave, per_wave, lane);
+    if (t * TR + TR <= Lk) {
+      stage_full_tile(p.k + kbase, sl, t * TR, kbuf(st), per_wave * wave, soff);
+      stage_full_tile(p.v + kbase, sl, t * TR, vbuf(st), per_wave * wave, soff);
+    } else {
+      stage_tile(p.k + kbase, sl, t * TR, Lk - 1, kbuf(st), per_wave * wave, per_wave, lane);
+      stage_tile(p.v + kbase, sl, t * TR, Lk - 1, vbuf(st), per_wave * wave, per_wave, lane);
+    }
   };
 
   // kMask: the tile holds keys past Lk (only the last one can)
