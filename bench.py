@@ -220,7 +220,7 @@ def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int)
     lk = [grid.n_video + x for x in wl.valid]
     o, lse = hv.hv_attention_fwd_lse(q, k, v, lk)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    delta = torch.empty(lse.numel() + hv.BWD_COUNTER_FLOATS, dtype=torch.float32, device=q.device)
+    delta = torch.empty(2 * lse.numel() + hv.BWD_COUNTER_FLOATS, dtype=torch.float32, device=q.device)
     ms_b = timed(torch, stream, lambda: hv.hv_joint_attention_bwd(
         q, k, v, o, v, lse, list(wl.valid), grid.n_video, dq=dq, dk=dk, dv=dv, delta=delta),
         max(2, reps // 2))

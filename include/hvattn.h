@@ -273,14 +273,16 @@ int hv_joint_attention_varlen_fwd(const hv_bf16* q, const hv_bf16* k, const hv_b
  *   text_valid_len, n_video, softmax_scale  as in hv_joint_attention_fwd
  *   dq, dk, dv          device pointers, layout *layout; must not overlap any
  *                       input or each other
- *   delta               device workspace of batch * 24 * seq_len floats plus
- *                       256 bytes (caller-owned, 4-byte aligned, disjoint from
- *                       all other arguments): the first part receives
- *                       -rowsum(dO * O) as fp32 [batch][24][seq_len]; the last
- *                       256 bytes hold the work counters through which the
- *                       two gradient kernels' persistent workgroups (one per
- *                       CU) take their blocks.  Its contents need no
- *                       initialisation; calls that share one race.
+ *   delta               device workspace of 2 * batch * 24 * seq_len floats
+ *                       plus 256 bytes (caller-owned, 4-byte aligned, disjoint
+ *                       from all other arguments): it receives
+ *                       -rowsum(dO * O), then -lse / softmax_scale, each as
+ *                       fp32 [batch][24][seq_len] (the starting accumulators
+ *                       of the dP and S products); the last 256 bytes hold
+ *                       the work counters through which the two gradient
+ *                       kernels' persistent workgroups (one per CU) take their
+ *                       blocks.  Its contents need no initialisation; calls
+ *                       that share one race.
  * Errors: HV_ERR_INVALID_ARG (NULL, valid length out of range, alignment,
  * overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
 int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
@@ -303,8 +305,8 @@ int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
  *   lse                 device fp32 [24][T], the forward's log-sum-exp as
  *                       hv_joint_attention_varlen_fwd writes it
  *   cu_seqlens_q/k, n_segments, softmax_scale  as in the forward
- *   delta               device workspace of 24 * T floats plus 256 bytes,
- *                       as in hv_joint_attention_bwd
+ *   delta               device workspace of 2 * 24 * T floats plus 256
+ *                       bytes, as in hv_joint_attention_bwd
  * Errors: HV_ERR_INVALID_ARG (NULL, batch != 1, bad offsets, alignment,
  * overlap), HV_ERR_UNSUPPORTED, HV_ERR_HIP. */
 int hv_joint_attention_varlen_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,

@@ -308,18 +308,18 @@ BWD_COUNTER_FLOATS = 64   # the 256 bytes of work counters after D in the backwa
 
 
 def _delta_workspace(delta, n_rows: int, device):
-    """The backward's delta workspace: n_rows * 24 floats of D, then the
-    counters.  A given tensor must be a contiguous float32 tensor with at least
-    that many elements."""
+    """The backward's delta workspace: n_rows * 24 floats of -D, as many of
+    -lse/scale, then the counters.  A given tensor must be a contiguous float32
+    tensor with at least that many elements."""
     import torch
 
-    need = n_rows * HV_HEADS + BWD_COUNTER_FLOATS
+    need = 2 * n_rows * HV_HEADS + BWD_COUNTER_FLOATS
     if delta is None:
         return torch.empty(need, dtype=torch.float32, device=device)
     if delta.dtype != torch.float32 or delta.device != device or not delta.is_contiguous() \
             or delta.numel() < need:
         raise ValueError(f"delta must be a contiguous float32 tensor of at least {need} elements "
-                         f"(24 per row, then {BWD_COUNTER_FLOATS} for the work counters)")
+                         f"(2 x 24 per row, then {BWD_COUNTER_FLOATS} for the work counters)")
     return delta
 
 

@@ -15,8 +15,8 @@
 // Three kernels, all MFMA 32x32x16 bf16 with fp32 accumulation:
 //   * delta: D per (row, head), one thread per 16-byte chunk, 16-lane DPP sum,
 //            stored negated: -D is where every dP accumulation starts, so the
-//            MFMAs yield dP - D directly (and the dkdv kernel's S chains start
-//            from -lse/scale, so the exponent is one multiply away);
+//            MFMAs yield dP - D directly; it also writes -lse/scale, where the
+//            dkdv kernel's S chains start, so the exponent is one multiply away;
 //   * dkdv:  one workgroup per (batch, head, 128 keys), 4 waves of 32 keys,
 //            K and V of its keys held in registers as MFMA operands; it walks
 //            all query tiles of 64 rows (Q, dO, lse, D staged in LDS by
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   const int b = (int)(row / p.seq_len);
   const int n = (int)(row - (int64_t)b * p.seq_len);
   const int64_t base = (int64_t)b * p.stride_b + (int64_t)n * p.stride_l + chunk * 8;
+  const float nis = -1.0f / p.scale;
   const u32x4* op = reinterpret_cast<const u32x4*>(p.o + base);
   const u32x4* gp = reinterpret_cast<const u32x4*>(p.dout + base);
 #pragma unroll
@@ -239,8 +240,13 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
         s = fmaf(__uint_as_float(ov[i][j] & 0xffff0000u), __uint_as_float(gv[i][j] & 0xffff0000u), s);
       }
       s = row16_sum(s);
-      // stored negated: it is the starting accumulator of the dP products
-      if (chunk == 0) p.delta[((int64_t)b * HV_HEADS + h0 + i) * p.seq_len + n] = -s;
+      // stored negated: it is the starting accumulator of the dP products;
+      // -lse/scale likewise starts the S products of the dK/dV kernel
+      if (chunk == 0) {
+        const int64_t at = ((int64_t)b * HV_HEADS + h0 + i) * p.seq_len + n;
+        p.delta[at] = -s;
+        p.nls[at] = p.lse[at] * nis;
+      }
     }
   }
 }
@@ -306,7 +312,6 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
 #pragma unroll
     for (int v = 0; v < 16; ++v) dk[dt][v] = dv[dt][v] = 0.f;
   const float c2 = p.scale_log2;
-  const float nis = -1.0f / p.scale;
   // a block of padded keys only has zero gradients: skip the query loop
   const int nq = kb * KV_KEYS >= Lk || L == 0 ? 0 : (L + TR - 1) / TR;
 
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
       stage_tile(p.q + qbase, sl, t * TR, L - 1, qbuf(st), 4 * wave, 4, lane);
       stage_tile(p.dout + qbase, sl, t * TR, L - 1, gbuf(st), 4 * wave, 4, lane);
     }
-    if (wave == 0) stage_vec(p.lse + vbase, t * TR, L - 1, lbuf(st), lane);
+    if (wave == 0) stage_vec(p.nls + vbase, t * TR, L - 1, lbuf(st), lane);
     if (wave == 1) stage_vec(p.delta + vbase, t * TR, L - 1, dbuf(st), lane);
   };
 
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r = 32 * u + 8 * g + 4 * hh;
-        const f32x4 l = *reinterpret_cast<const f32x4*>(lt + r) * nis;
+        const f32x4 l = *reinterpret_cast<const f32x4*>(lt + r);  // -lse/scale
         const f32x4 d = *reinterpret_cast<const f32x4*>(dtv + r);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -669,8 +674,10 @@ hipError_t launch_attn_bwd(BwdParams& p, hipStream_t stream) {
   p.n_q_blocks = qblocks;
   p.n_kv_blocks = kblocks;
   if (qblocks == 0 && kblocks == 0) return hipSuccess;
-  // the two work counters follow D in the caller's workspace
-  p.counters = reinterpret_cast<int*>(p.delta + (int64_t)p.batch * HV_HEADS * p.seq_len);
+  // the caller's workspace: -D, then -lse/scale, then the two work counters
+  const int64_t nrows = (int64_t)p.batch * HV_HEADS * p.seq_len;
+  p.nls = p.delta + nrows;
+  p.counters = reinterpret_cast<int*>(p.delta + 2 * nrows);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

@@ -190,7 +190,8 @@ struct BwdParams {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;    // natural log, per (head, row) as the segments place it
-  float* delta;        // same placement, written by the first kernel
+  float* delta;        // -D, same placement, written by the first kernel
+  float* nls;          // -lse / scale, same placement, written by the first kernel
   int* counters;       // next block of the dK/dV [0] and dQ [1] persistent workgroups
   uint16_t* dq;
   uint16_t* dk;

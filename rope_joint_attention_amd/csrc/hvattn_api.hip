@@ -93,7 +93,7 @@ float scale_log2(float softmax_scale) {
 
 // Pointers, alignment and overlap of the backward's arguments (shared by the
 // padded and the packed forms).  lse holds batch * 24 * seq_len floats; delta
-// as many, followed by 256 bytes of work counters.
+// twice as many, followed by 256 bytes of work counters.
 int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, const hv_bf16* out,
                       const hv_bf16* dout, const float* lse, hv_bf16* dq, hv_bf16* dk, hv_bf16* dv,
                       float* delta, const hv_layout* layout) {
@@ -115,7 +115,7 @@ int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, cons
       if (overlap(outs[i], outs[j], layout, extent)) return HV_ERR_INVALID_ARG;
   }
   const uintptr_t vb = (uintptr_t)layout->batch * HV_HEADS * layout->seq_len * sizeof(float);
-  const uintptr_t db = vb + hv::kCounterBytes;  // D, then the two kernels' work counters
+  const uintptr_t db = 2 * vb + hv::kCounterBytes;  // -D, -lse/scale, the two work counters
   const uintptr_t tb = (uintptr_t)extent * sizeof(hv_bf16);
   if (ranges_meet(delta, db, lse, vb)) return HV_ERR_INVALID_ARG;
   for (const hv_bf16* t : ins)

@@ -383,7 +383,7 @@ def test_backward_validation(kwargs, expect):
     assert bwd(**kwargs) == expect
 
 
-D_BYTES = 24 * 300 * 4       # D of the default layout; 256 bytes of work counters follow it
+D_BYTES = 2 * 24 * 300 * 4   # -D and -lse/scale of the default layout; 256 bytes of counters follow
 
 
 def test_backward_delta_includes_the_counters():

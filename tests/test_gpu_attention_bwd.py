@@ -103,16 +103,18 @@ def test_bwd_poisoned_padding_and_determinism():
 
 
 def test_bwd_workspace_holds_d_then_the_counters():
-    # the delta workspace: D = rowsum(dO * O) per (batch, head, row) in fp32,
-    # then the work counters of the two persistent gradient kernels (each ends
-    # at blocks + workgroups: every workgroup's last take finds no block); the
-    # rest of the 256 counter bytes is not written.  A second, smaller call
-    # reuses the workspace without clearing it.
+    # the delta workspace: -D = -rowsum(dO * O) per (batch, head, row) in fp32,
+    # then -lse/scale in the same placement, then the work counters of the two
+    # persistent gradient kernels (each ends at blocks + workgroups: every
+    # workgroup's last take finds no block); the rest of the 256 counter bytes
+    # is not written.  A second, smaller call reuses the workspace without
+    # clearing it.
     import torch
     import rope_joint_attention_amd as hv
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    ws = torch.full((2 * 24 * 700 + hv.BWD_COUNTER_FLOATS,), 7.0, dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(128.0)
+    ws = torch.full((2 * 2 * 24 * 700 + hv.BWD_COUNTER_FLOATS,), 7.0, dtype=torch.float32, device="cuda")
     for B, L, N, valid, seed in ((2, 700, 640, (60, 13), 61), (1, 129, 100, (29,), 62)):
         bits, dout = draw(B, L, seed=seed)
         q, k, v = (bits_to_torch(bits[n]) for n in "qkv")
@@ -126,12 +128,13 @@ def test_bwd_workspace_holds_d_then_the_counters():
         d_ref = (out.float() * g.float()).sum(-1).permute(0, 2, 1).reshape(-1).cpu().numpy()
         got = ws.cpu().numpy()
         np.testing.assert_allclose(-got[:n], d_ref, rtol=1e-5, atol=1e-5)
-        cnt = got[n:n + 2].view(np.int32)
+        np.testing.assert_allclose(got[n:2 * n], -lse.cpu().numpy().reshape(-1) / scale, rtol=1e-6)
+        cnt = got[2 * n:2 * n + 2].view(np.int32)
         kb, qb = B * 24 * ((L + 127) // 128), B * 24 * ((L + 255) // 256)
         assert cnt[0] == kb + min(kb, cus) and cnt[1] == qb + min(qb, cus), (cnt, kb, qb)
         if B == 2:
-            assert (got[n + 2:n + hv.BWD_COUNTER_FLOATS] == 7.0).all()
-            assert (got[n + hv.BWD_COUNTER_FLOATS:] == 7.0).all()
+            assert (got[2 * n + 2:2 * n + hv.BWD_COUNTER_FLOATS] == 7.0).all()
+            assert (got[2 * n + hv.BWD_COUNTER_FLOATS:] == 7.0).all()
 
 
 @pytest.mark.timeout(600)

@@ -31,7 +31,7 @@ def test_graph_replays_match_eager_calls():
     lse = torch.empty((B, hv.HV_HEADS, L), dtype=torch.float32, device="cuda")
     ws = torch.empty(hv.hv_attention_workspace_bytes(B * L, B), dtype=torch.uint8, device="cuda")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    delta = torch.empty(B * hv.HV_HEADS * L + hv.BWD_COUNTER_FLOATS, dtype=torch.float32, device="cuda")
+    delta = torch.empty(2 * B * hv.HV_HEADS * L + hv.BWD_COUNTER_FLOATS, dtype=torch.float32, device="cuda")
 
     def fill(seed):
         bits = hvinputs.draw_qkv(B, L, seed)
