@@ -506,7 +506,7 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
   auto vbuf = [&](auto st) -> unsigned char* { if constexpr (decltype(st)::value == 0) return sV0; else return sV1; };
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: DMA destinations (M0) from the scalar unit
   const int l32 = lane & 31;
   const int hh = lane >> 5;
 
