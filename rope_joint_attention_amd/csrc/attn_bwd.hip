@@ -17,14 +17,14 @@
 //            stored negated: -D is where every dP accumulation starts, so the
 //            MFMAs yield dP - D directly; it also writes -lse/scale, where the
 //            dkdv kernel's S chains start, so the exponent is one multiply away;
-//   * dkdv:  one workgroup per (batch, head, 128 keys), 4 waves of 32 keys,
+//   * dkdv:  a block is (batch, head, 128 keys), 4 waves of 32 keys,
 //            K and V of its keys held in registers as MFMA operands; it walks
 //            all query tiles of 64 rows (Q, dO, lse, D staged in LDS by
 //            global->LDS loads, two stages) and accumulates dV^T += dO^T P and
 //            dK^T += Q^T dS in registers; the two 32-query units of a tile
 //            are staggered so one unit's exp/dS work runs under the other's
 //            MFMAs;
-//   * dq:    one workgroup per (batch, head, 256 queries), 8 waves of 32
+//   * dq:    a block is (batch, head, 256 queries), 8 waves of 32
 //            queries (two per SIMD) with Q and dO in registers; it walks the key tiles of 64
 //            rows (K, V staged the same way) and accumulates dQ^T += K^T dS^T.
 // The dkdv and dq grids are persistent: one workgroup per CU, each taking
