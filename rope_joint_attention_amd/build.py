@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
     "-mcode-object-version=5",
     # no packed fp32 VALU ops in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMAs accumulate in VGPRs: the dK/dV kernel keeps its K/V operands in
+    # AGPRs and its score accumulators in VGPRs, where the softmax reads them
+    # (the other kernels' code is the same either way)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

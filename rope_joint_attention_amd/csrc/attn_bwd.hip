@@ -300,6 +300,10 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     for (int kc = 0; kc < 8; ++kc) {
       kf[kc] = *reinterpret_cast<const bf16x8*>(p.k + r + kc * 16);
       vf[kc] = *reinterpret_cast<const bf16x8*>(p.v + r + kc * 16);
+      // K and V are only ever MFMA operands: keep them in AGPRs, which
+      // leaves the VGPRs to the accumulators (with VGPR-form MFMAs the
+      // softmax then reads S and dP without a copy per value)
+      asm volatile("" : "+a"(kf[kc]), "+a"(vf[kc]));
     }
   }
   int roff[8], troff[8];
