@@ -394,7 +394,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     // the same for unit 1, with the probabilities and dS of unit 0 computed
     // under them; 16..23 dV, dK of unit 0 (transposed dO, Q) with unit 1's
     // softmax under them; 24..31 dV, dK of unit 1.  Each pair's two LDS
-    // operands are read one pair ahead, the row statistics four pairs ahead.
+    // operands are read two pairs ahead, the row statistics four pairs ahead.
     auto ops = [&](int i, bf16x8& a, bf16x8& b) __attribute__((always_inline)) {
       if (i < 16) {
         const int kc = i & 7, row0 = 32 * (i >> 3);
@@ -407,13 +407,14 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
         b = tr_operand(qt, troff, dt, 32 * u + 16 * mm);
       }
     };
-    bf16x8 ca, cb, na, nb, pb0[2], db0[2], pb1[2], db1[2];
+    bf16x8 ca, cb, na, nb, xa, xb, pb0[2], db0[2], pb1[2], db1[2];
     ops(0, ca, cb);
+    ops(1, na, nb);
     stats(0);
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < 32) ops(i + 1, na, nb);
+      if (i + 2 < 32) ops(i + 2, xa, xb);
       if (i == 4) stats(1);
       if (i == 16) {
         pb0[0] = words(pw[0], 0); pb0[1] = words(pw[0], 1);
@@ -443,6 +444,8 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
       }
       ca = na;
       cb = nb;
+      na = xa;
+      nb = xb;
     }
     __builtin_amdgcn_sched_barrier(0);
   };
