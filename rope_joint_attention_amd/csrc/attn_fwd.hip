@@ -438,8 +438,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   //            the rest two chunks ahead), each followed by exp2 / bf16 / sum
   //            work for keys 0..31 of tile t;
   //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead); the first
-  //            eight carry the exp2 work for keys 32..63, the next four the row
-  //            maximum of tile t+1;
+  //            ten carry the exp2 work for keys 32..63 (with the two packs in
+  //            slots of their own), the last eight the row maximum of tile t+1,
+  //            so the VALU work is spread over the whole phase;
   //   then the first K operands of tile t+2, requests for K tile t+4 and V
   //   tile t+3, the first chunk of QK^T MFMAs of tile t+2 (into the score
   //   registers of tile t, free by then), so that the MFMA pipe has work
@@ -488,18 +489,17 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       const int mm = i >> 2, dt = i & 3;
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 1], pb[mm], o[dt], 0, 0, 0);
       if (i + 2 < 16) vf[i & 1] = v_frag(VS{}, (i + 2) & 3, (i + 2) >> 2);
-      if (i < 8) {  // keys 32..63 of tile t, ready before PV chunks 2 and 3
-        exp_pair(cur, 16 + 2 * i);
-        if (i == 3) pb[2] = pack_p(cur, 2);
-        if (i == 7) pb[3] = pack_p(cur, 3);
-      }
-      if (i >= 8 && i < 12) {  // row maximum of tile t+1, in four slices of one chain
+      // keys 32..63 of tile t, packed before PV chunks 2 and 3 need them
+      if (i < 4) exp_pair(cur, 16 + 2 * i);
+      if (i == 4) pb[2] = pack_p(cur, 2);
+      if (i >= 5 && i < 9) exp_pair(cur, 16 + 2 * (i - 1));
+      if (i == 9) pb[3] = pack_p(cur, 3);
+      if (i >= 8) {  // row maximum of tile t+1, in eight pieces of one chain
         const int j = i - 8;
-        const f32x16& sv = nxt[j >> 1];
-        const int b = 8 * (j & 1);
+        const f32x16& sv = nxt[j >> 2];
+        const int b = 4 * (j & 3);
         float m = j ? vmax(vmax(part_run, sv[b]), sv[b + 1]) : vmax(sv[b], sv[b + 1]);
-#pragma unroll
-        for (int v = 2; v < 8; v += 2) m = vmax(vmax(m, sv[b + v]), sv[b + v + 1]);
+        m = vmax(vmax(m, sv[b + 2]), sv[b + 3]);
         part_run = m;
       }
     }
