@@ -435,8 +435,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // compiler from regrouping):
   //   phase 1: QK^T MFMAs of tile t+1 (its first chunk was issued before the
   //            previous barrier, the operands of the next two were read there,
-  //            the rest two chunks ahead), each followed by exp2 / bf16 / sum
-  //            work for keys 0..31 of tile t;
+  //            the rest two chunks ahead), interleaved with the exp2 / bf16 /
+  //            sum work for keys 0..31 of tile t, spread evenly over the chunks;
   //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead); the first
   //            ten carry the exp2 work for keys 32..63 (with the two packs in
   //            slots of their own), the last eight the row maximum of tile t+1,
@@ -464,8 +464,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);
       const int sl0 = 2 * (kc & 1);
       nxt[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0], qf[kc], nxt[0], 0, 0, 0);
-      if (kc == 1) exp_pair(cur, 0);
-      exp_pair(cur, 2 * kc);  // keys 0..31 of tile t (score registers 0..15 of cur[0])
+      // keys 0..31 of tile t: pairs 0,1 | 2,3 | pack | 4 | 5 | 6,7 | pack
+      if (kc == 1) { exp_pair(cur, 0); exp_pair(cur, 2); }
+      if (kc == 2) { exp_pair(cur, 4); exp_pair(cur, 6); }
+      if (kc == 4) exp_pair(cur, 8);
+      if (kc == 5) exp_pair(cur, 10);
+      if (kc == 6) { exp_pair(cur, 12); exp_pair(cur, 14); }
       nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0 + 1], qf[kc], nxt[1], 0, 0, 0);
       if (kc == 3) pb[0] = pack_p(cur, 0);
       if (kc == 7) pb[1] = pack_p(cur, 1);
