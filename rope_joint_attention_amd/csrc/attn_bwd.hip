@@ -341,7 +341,8 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   //   A0 | A1 + V0 | B0 + V1 | B1
   // kMask: the tile may hold query rows past L or this block keys past Lk.
   // Full tiles of a block whose keys are all valid skip the per-element mask.
-  auto tile = [&](auto st, auto masked, int t) {
+  // mid: called once inside the tile (the next tile's request, or nothing).
+  auto tile = [&](auto st, auto masked, int t, auto mid) {
     constexpr bool kMask = decltype(masked)::value;
     const unsigned char* qt = qbuf(st);
     const unsigned char* gt = gbuf(st);
@@ -415,6 +416,7 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
     for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       if (i + 2 < 32) ops(i + 2, xa, xb);
+      if (i == 6) mid();  // the next tile's request (measured: cheapest at pair 6)
       if (i == 4) stats(1);
       if (i == 16) {
         pb0[0] = words(pw[0], 0); pb0[1] = words(pw[0], 1);
@@ -458,25 +460,27 @@ __global__ __launch_bounds__(KV_WAVES * 64, 1) void attn_bwd_dkdv_kernel(BwdPara
   const int n_unmasked = (kb + 1) * KV_KEYS <= Lk ? L / TR : 0;
   if (nq > 0) load(I0{}, 0);
   int t = 0;
+  // In the unmasked loop the next tile is requested from inside the tile (at
+  // its seventh MFMA pair) rather than right after the barrier: its stage was
+  // freed by that barrier either way, and the later request costs less.
+  auto none = [] {};
   for (; t + 2 <= n_unmasked; t += 2) {
     barrier_loads_done();
-    load(I1{}, t + 1);
-    tile(I0{}, Unmasked{}, t);
+    tile(I0{}, Unmasked{}, t, [&] { load(I1{}, t + 1); });
     barrier_loads_done();
-    if (t + 2 < nq) load(I0{}, t + 2);
-    tile(I1{}, Unmasked{}, t + 1);
+    tile(I1{}, Unmasked{}, t + 1, [&] { if (t + 2 < nq) load(I0{}, t + 2); });
   }
   for (; t + 2 <= nq; t += 2) {
     barrier_loads_done();
     load(I1{}, t + 1);
-    tile(I0{}, Masked{}, t);
+    tile(I0{}, Masked{}, t, none);
     barrier_loads_done();
     if (t + 2 < nq) load(I0{}, t + 2);
-    tile(I1{}, Masked{}, t + 1);
+    tile(I1{}, Masked{}, t + 1, none);
   }
   if (t < nq) {
     barrier_loads_done();
-    tile(I0{}, Masked{}, t);
+    tile(I0{}, Masked{}, t, none);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
@@ -581,8 +585,9 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
     }
   };
 
-  // kMask: the tile holds keys past Lk (only the last one can)
-  auto tile = [&](auto st, auto masked, int t) {
+  // kMask: the tile holds keys past Lk (only the last one can); mid: called
+  // once between the two halves (the next tile's request, or nothing)
+  auto tile = [&](auto st, auto masked, int t, auto mid) {
     constexpr bool kMask = decltype(masked)::value;
     const unsigned char* kt = kbuf(st);
     const unsigned char* vt = vbuf(st);
@@ -591,6 +596,7 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
     // registers, so two waves share each SIMD)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      if (h == 1) mid();  // the next tile's request, between the halves (measured)
       // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
       f32x16 s, dp;
 #pragma unroll
@@ -625,26 +631,27 @@ __global__ __launch_bounds__(Q_WAVES * 64, 1) void attn_bwd_dq_kernel(BwdParams 
   const int n_full = Lk / TR;  // key tiles with every key valid
   load(I0{}, 0);
   int t = 0;
+  // In the loop over full tiles the next tile is requested between the two
+  // halves of the tile rather than right after the barrier (cheaper, measured).
+  auto none = [] {};
   for (; t + 2 <= n_full; t += 2) {
     barrier_loads_done();
-    load(I1{}, t + 1);
-    tile(I0{}, Unmasked{}, t);
+    tile(I0{}, Unmasked{}, t, [&] { load(I1{}, t + 1); });
     barrier_loads_done();
-    if (t + 2 < nk) load(I0{}, t + 2);
-    tile(I1{}, Unmasked{}, t + 1);
+    tile(I1{}, Unmasked{}, t + 1, [&] { if (t + 2 < nk) load(I0{}, t + 2); });
   }
   // at most one full tile and the partial one remain
   for (; t + 2 <= nk; t += 2) {
     barrier_loads_done();
     load(I1{}, t + 1);
-    tile(I0{}, Masked{}, t);
+    tile(I0{}, Masked{}, t, none);
     barrier_loads_done();
     if (t + 2 < nk) load(I0{}, t + 2);
-    tile(I1{}, Masked{}, t + 1);
+    tile(I1{}, Masked{}, t + 1, none);
   }
   if (t < nk) {
     barrier_loads_done();
-    tile(I0{}, Masked{}, t);
+    tile(I0{}, Masked{}, t, none);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 
