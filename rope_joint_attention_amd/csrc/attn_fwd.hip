@@ -440,13 +440,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead); the first
   //            ten carry the exp2 work for keys 32..63 (with the two packs in
   //            slots of their own), the last eight the row maximum of tile t+1,
-  //            so the VALU work is spread over the whole phase; the requests
-  //            for K tile t+4 and V tile t+3 go out at its 13th and 15th MFMA;
-  //   then the first K operands of tile t+2, the first chunk of QK^T MFMAs of
-  //   tile t+2 (into the score registers of tile t, free by then), so that
-  //   the MFMA pipe has work queued while the waves meet at the barrier, and
-  //   the operands of its second and third chunks; one barrier and the
-  //   reference update.
+  //            so the VALU work is spread over the whole phase; the first K
+  //            operands of tile t+2 are read at its 11th MFMA and the requests
+  //            for K tile t+4 and V tile t+3 go out at its 13th and 15th;
+  //   then the first chunk of QK^T MFMAs of tile t+2 (into the score
+  //   registers of tile t, free by then), so that the MFMA pipe has work
+  //   queued while the waves meet at the barrier, and the operands of its
+  //   second and third chunks; one barrier and the reference update.
   // K tile t+1 and V tile t were requested three steps earlier (or in the
   // prologue); every barrier waits for the loads of the step before it, so a
   // tile is complete and visible from the barrier that follows its request
@@ -504,6 +504,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       // phase, where they cost least (measured)
       if (i == 12) load_k(KL{}, min(t + KAHEAD, ntiles - 1));
       if (i == 14) load_v(VL{}, min(t + VAHEAD, ntiles - 1));
+      if (i == 10) {  // first K operands of tile t+2 (the QK^T phase is done with kf)
+        kf[0] = k_frag(KN{}, 0, 0);
+        kf[1] = k_frag(KN{}, 1, 0);
+        kf[2] = k_frag(KN{}, 0, 1);
+        kf[3] = k_frag(KN{}, 1, 1);
+      }
       if (i >= 8) {  // row maximum of tile t+1, in eight pieces of one chain
         const int j = i - 8;
         const f32x16& sv = nxt[j >> 2];
@@ -513,11 +519,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         part_run = m;
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    kf[0] = k_frag(KN{}, 0, 0);
-    kf[1] = k_frag(KN{}, 1, 0);
-    kf[2] = k_frag(KN{}, 0, 1);
-    kf[3] = k_frag(KN{}, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     const float mx = max_across_halves(part_run) * c2;
     __builtin_amdgcn_sched_barrier(0);
