@@ -437,10 +437,11 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   //            previous barrier, the operands of the next two were read there,
   //            the rest two chunks ahead), interleaved with the exp2 / bf16 /
   //            sum work for keys 0..31 of tile t, spread evenly over the chunks;
-  //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead); the first
-  //            ten carry the exp2 work for keys 32..63 (with the two packs in
-  //            slots of their own), the last eight the row maximum of tile t+1,
-  //            so the VALU work is spread over the whole phase; the first K
+  //   phase 2: PV MFMAs of tile t (V operands read two MFMAs ahead, the first
+  //            two already during phase 1); the first ten carry the exp2
+  //            work for keys 32..63 (with the two packs in slots of their
+  //            own), the last eight the row maximum of tile t+1, so the VALU
+  //            work is spread over the whole phase; the first K
   //            operands of tile t+2 are read at its 11th MFMA and the requests
   //            for K tile t+4 and V tile t+3 go out at its 13th and 15th;
   //   then the first chunk of QK^T MFMAs of tile t+2 (into the score
@@ -460,6 +461,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     using VL = std::integral_constant<int, (U + 3) % NSTAGE>;   // V tile t+3 goes here
     refresh_offsets();
     bf16x8 pb[4];
+    bf16x8 vf[2];  // V operands, two MFMAs ahead in the PV phase
 #pragma unroll
     for (int kc = 1; kc < 8; ++kc) {  // chunk 0 was issued before the barrier
       __builtin_amdgcn_sched_barrier(0);
@@ -472,6 +474,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       if (kc == 5) exp_pair(cur, 10);
       if (kc == 6) { exp_pair(cur, 12); exp_pair(cur, 14); }
       nxt[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sl0 + 1], qf[kc], nxt[1], 0, 0, 0);
+      if (kc == 5) {  // the first two V operands of the PV phase (tile t is visible)
+        vf[0] = v_frag(VS{}, 0, 0);
+        vf[1] = v_frag(VS{}, 1, 0);
+      }
       if (kc == 3) pb[0] = pack_p(cur, 0);
       if (kc == 7) pb[1] = pack_p(cur, 1);
       if (kc + 2 < 8) {
@@ -484,9 +490,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     asm volatile("" ::"v"(pb[0]), "v"(pb[1]));
     if (t + 2 == ntiles) mask_tile(nxt[0], nxt[1], Lk - (t + 1) * BN, hh);
 
-    bf16x8 vf[2];
-    vf[0] = v_frag(VS{}, 0, 0);
-    vf[1] = v_frag(VS{}, 1, 0);
     float part_run = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
