@@ -31,7 +31,10 @@ Each function restates, in NumPy float64, what the HunyuanVideo notes page
                       report summary page's training-side attention cost),
                       by the chain rule through the softmax
                       (``joint_attention_bwd_dq_rows``: dQ of selected rows;
-                      ``varlen_attention_bwd``: the same over packed segments);
+                      ``joint_attention_bwd_by_rows``: all three for long
+                      sequences, the key gradients summed over chunks of
+                      query rows; ``varlen_attention_bwd``: the same over
+                      packed segments);
 * ``hot_path``        token grid, RoPE and attention in sequence.
 
 Nothing here is blocked, fused or reordered beyond the formulas: the matrix
@@ -66,6 +69,7 @@ from .hv_oracle import (  # noqa: F401
     varlen_attention,
     joint_attention_bwd,
     joint_attention_bwd_dq_rows,
+    joint_attention_bwd_by_rows,
     varlen_attention_bwd,
     hot_path,
 )

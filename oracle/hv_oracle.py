@@ -352,6 +352,91 @@ def joint_attention_bwd_dq_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dou
     return dq
 
 
+def joint_attention_bwd_by_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                                n_video: int, valid: Sequence[int], scale: Optional[float] = None,
+                                heads: Optional[Sequence[int]] = None,
+                                batches: Optional[Sequence[int]] = None, chunk: int = 256,
+                                workers: int = 1):
+    """Gradients of ``joint_attention_bwd`` for long sequences, float64.
+
+    The same chain rule, written per query row i of one (batch, head) over the
+    valid keys j (the report summary page's training-side attention, the
+    forward of notes page section 5.2):
+        P_i   = softmax_j(scale * q_i . k_j)     (the whole row, every valid key)
+        dP_ij = dO_i . v_j,   D_i = sum_j P_ij dP_ij,   dS_ij = P_ij (dP_ij - D_i)
+        dQ_i  = scale * sum_j dS_ij k_j
+    while each key gradient is a sum over the query rows,
+        dV_j = sum_i P_ij dO_i,   dK_j = scale * sum_i dS_ij q_i,
+    so it is added up over consecutive chunks of ``chunk`` query rows, in
+    chunk order.  Only a chunk x L_k block of P is held per chunk, which is
+    what lets the oracle check every gradient element at the longest
+    workloads (one L x L_k matrix there is over 100 GB).  Padded keys get
+    zero dK, dV.  ``workers`` > 1 computes that many chunks at once on
+    threads (single-threaded BLAS each); the sums are still taken in chunk
+    order (only the rounding inside the library's matrix products can
+    differ with the thread count).
+
+    ``q``, ``k``, ``v``, ``dout``: [B, L, H, D].  Returns (dq, dk, dv), each
+    [len(batches), L, len(heads), D] for the listed batch entries and heads.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    B, L, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    heads = list(range(H)) if heads is None else list(heads)
+    batches = list(range(B)) if batches is None else list(batches)
+    shape = (len(batches), L, len(heads), D)
+    dq, dk, dv = (np.zeros(shape, dtype=np.float64) for _ in range(3))
+
+    def one_chunk(qc, gc, kb, vb):
+        p = (qc @ kb.T) * scale
+        p -= p.max(axis=1, keepdims=True)
+        np.exp(p, out=p)
+        p /= p.sum(axis=1, keepdims=True)
+        dp = gc @ vb.T
+        d = (p * dp).sum(axis=1, keepdims=True)
+        dp -= d
+        dp *= p                                   # dS of the chunk
+        return scale * (dp @ kb), scale * (dp.T @ qc), p.T @ gc
+
+    limit = None
+    if workers > 1:
+        try:
+            from threadpoolctl import threadpool_limits
+            limit = threadpool_limits(1)
+        except ImportError:  # pragma: no cover
+            limit = None
+    try:
+        with ThreadPoolExecutor(max_workers=max(1, workers)) as pool:
+            for bi, b in enumerate(batches):
+                lk = n_video + int(valid[b])
+                if lk <= 0:
+                    raise ValueError("no valid keys")
+                for hi, h in enumerate(heads):
+                    kb = np.ascontiguousarray(k[b, :lk, h, :], dtype=np.float64)
+                    vb = np.ascontiguousarray(v[b, :lk, h, :], dtype=np.float64)
+                    starts = list(range(0, L, chunk))
+                    pending = []
+                    for i in range(len(starts) + 1):
+                        if i < len(starts):
+                            s0 = starts[i]
+                            qc = np.ascontiguousarray(q[b, s0:s0 + chunk, h, :], dtype=np.float64)
+                            gc = np.ascontiguousarray(dout[b, s0:s0 + chunk, h, :], dtype=np.float64)
+                            pending.append((s0, pool.submit(one_chunk, qc, gc, kb, vb)))
+                        # consume in chunk order, keeping at most 2 x workers in flight
+                        while pending and (len(pending) > 2 * max(1, workers) or i == len(starts)):
+                            s0, fut = pending.pop(0)
+                            dqc, dkc, dvc = fut.result()
+                            dq[bi, s0:s0 + chunk, hi, :] = dqc
+                            dk[bi, :lk, hi, :] += dkc
+                            dv[bi, :lk, hi, :] += dvc
+    finally:
+        if limit is not None:
+            limit.unregister() if hasattr(limit, "unregister") else limit.restore_original_limits()
+    return dq, dk, dv
+
+
 def varlen_attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
                          cu_q: Sequence[int], cu_k: Sequence[int],
                          scale: Optional[float] = None,

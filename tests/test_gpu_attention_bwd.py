@@ -9,7 +9,9 @@ no NaN/Inf; the kernel rounds P and dS to bf16 as MFMA operands (2^-9
 relative each, averaging out) and reads O in bf16, so a correct kernel sits
 near 2e-3 relative.  Sizes are floored at 1e-3 per element, so an exactly-zero
 reference gradient (a single key) is held to rounding noise below 2e-5.
-Padded keys must get exactly zero dK, dV.
+Padded keys must get exactly zero dK, dV.  At the workload sizes whole heads
+are compared on every row and key (the oracle's query-chunked gradients
+never hold an L x L matrix).
 """
 import numpy as np
 import pytest
@@ -151,14 +153,28 @@ def test_bwd_image_workload_full():
         log(f"  {name} {grad_close(widen(got), r, name)}")
 
 
+# Heads (and batch entries) compared element by element on every row at the
+# full workload sizes, with the query-chunked fp64 gradients of the oracle.
+FULL_GRAD_HEADS = {
+    "video_544x960x17": ([0, 13], [0]),
+    "video_720x1280x33_b2": ([0, 13], [0, 1]),
+    "video_544x960x129": ([5], [0]),
+    "video_720x1280x129": ([17], [0]),
+}
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["video_544x960x17", "video_720x1280x33_b2", "video_544x960x129",
                                   "video_720x1280x129"])
 def test_bwd_workloads(name):
-    # dQ on sampled rows against the oracle row by row; dK and dV on every row
+    # dQ, dK and dV of the listed heads on every row and key against the
+    # oracle; dQ of three heads on sampled rows; dK and dV of every head
     # through identities that hold at any size (the key gradients of each
-    # (batch, head) sum to zero; the value gradients sum to the summed dO),
-    # plus all rows of two heads against the full oracle where it is cheap.
+    # (batch, head) sum to zero, the value gradients sum to the summed dO).
+    import os
+
+    from oracle import joint_attention_bwd_by_rows
+
     wl = hvinputs.WORKLOADS[name]
     g = token_grid(wl.frames, wl.height, wl.width)
     L = g.n_video + wl.text_capacity
@@ -170,6 +186,7 @@ def test_bwd_workloads(name):
     ref = joint_attention_bwd_dq_rows(widen(bits["q"][:, rows]), widen(bits["k"]), widen(bits["v"]),
                                       widen(dout[:, rows]), g.n_video, wl.valid, heads=heads)
     log(f"  dq rows {grad_close(widen(dq[:, rows][:, :, heads]), ref, 'dq rows')}")
+    del ref
     for b in range(wl.batch):
         n = g.n_video + wl.valid[b]
         dkb = widen(dk[b, :n]).sum(axis=0)              # [24, 128]
@@ -180,11 +197,15 @@ def test_bwd_workloads(name):
         err = np.abs(dvb - gsum)
         assert np.all(err <= 1e-2 * np.abs(widen(dv[b, :n])).sum(axis=0) + 1e-3), float(err.max())
         assert not widen(dk[b, n:]).any() and not widen(dv[b, n:]).any()
-    if L <= 11000:
-        full = joint_attention_bwd(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), widen(dout),
-                                   g.n_video, wl.valid, heads=[0, 13])
+    fh, fb = FULL_GRAD_HEADS[name]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    for h in fh:
+        sub = [t[:, :, h:h + 1] for t in (bits["q"], bits["k"], bits["v"], dout)]
+        full = joint_attention_bwd_by_rows(*(widen(t) for t in sub), g.n_video, wl.valid,
+                                           batches=fb, workers=workers)
         for i, (nm, got) in enumerate((("dq", dq), ("dk", dk), ("dv", dv))):
-            log(f"  {nm} heads 0,13 {grad_close(widen(got[:, :, [0, 13]]), full[i], nm)}")
+            e = grad_close(widen(got[fb][:, :, h:h + 1]), full[i], f"{nm} head {h}")
+            log(f"  {nm} head {h} batch {fb} all rows {e}")
 
 
 def test_bwd_maximum_batch():

@@ -154,3 +154,44 @@ def test_varlen_bwd_matches_per_clip_joint_gradients():
         ref = joint_attention_bwd(q[None, a:b], k[None, a:b], v[None, a:b], g[None, a:b], b - a, [0])
         for got, want in zip((dq, dk, dv), ref):
             assert np.allclose(got[a:b], want[0], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("chunk,workers", [(1, 1), (3, 1), (7, 4), (256, 1)])
+def test_by_rows_matches_the_full_gradient(chunk, workers):
+    # the query-chunked form must equal the one-matrix form for every chunk
+    # size, ragged last chunks included, on selected batch entries and heads
+    from oracle import joint_attention_bwd_by_rows
+
+    q, k, v, g, N, valid = setup(13, B=3, L=23, H=3, N=17, valid=(6, 0, 4), qs=2.0)
+    ref = joint_attention_bwd(q, k, v, g, N, valid, heads=[2, 0])
+    got = joint_attention_bwd_by_rows(q, k, v, g, N, valid, heads=[2, 0], batches=[2, 0],
+                                      chunk=chunk, workers=workers)
+    for want, have in zip(ref, got):
+        assert np.allclose(have, want[[2, 0]], rtol=1e-12, atol=1e-13)
+
+
+def test_by_rows_finite_differences_sums_and_padding():
+    from oracle import joint_attention_bwd_by_rows
+
+    q, k, v, g, N, valid = setup(14, B=2, L=11, N=8, valid=(3, 1), qs=1.5)
+    dq, dk, dv = joint_attention_bwd_by_rows(q, k, v, g, N, valid, chunk=4)
+    r = np.random.default_rng(15)
+    eps = 1e-6
+    for name, t, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(10):
+            idx = tuple(int(r.integers(0, n)) for n in t.shape)
+            if name != "q" and idx[1] >= N + valid[idx[0]]:
+                continue
+            old = t[idx]
+            t[idx] = old + eps
+            lp = loss(q, k, v, g, N, valid)
+            t[idx] = old - eps
+            lm = loss(q, k, v, g, N, valid)
+            t[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    for b in range(2):
+        n = N + valid[b]
+        assert not dk[b, n:].any() and not dv[b, n:].any()
+        assert np.allclose(dk[b].sum(axis=0), 0.0, atol=1e-12)
+        assert np.allclose(dv[b].sum(axis=0), g[b].sum(axis=0), rtol=1e-12, atol=1e-12)
