@@ -8,9 +8,12 @@ hv_token_grid -> hv_rope3d_apply (video Q/K, in place) -> hv_joint_attention_fwd
 (with its packed-V workspace: the call packs V, then runs the attention; the
 attention time reported covers both kernels, so the roofline figure slightly
 understates the attention kernel alone).
-Inputs are generated on the host, copied to HBM before timing, and stay
-resident.  RoPE works in place, so step i rotates the output of step i-1: the
-same bytes and arithmetic as a fresh batch.
+Inputs are generated on the host and copied to HBM before timing.  RoPE
+works in place, so every step gets a fresh batch: warmup + steps copies of
+the unrotated Q and K are staged in HBM beforehand (33.6 GB at
+720x1280x129 with the defaults; the part has 288 GB), and step i rotates copy
+i and runs the attention on it.  V, the output and the workspace are shared.
+The JSON records the SHA-256 of the input bytes and the host's core count.
 
 Printed: ONE JSON line (stdout) with the whole-step throughput in attention
 TFLOP/s (algorithmic FLOPs 4*heads*head_dim*sum_b L*Lk_b over the step time),
@@ -86,6 +89,7 @@ def cpu_baseline(bits, wl, n_video, seq_len, rows_n: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    nproc = host_cores()
     rng = np.random.Generator(np.random.PCG64(wl.seed))
     rows = np.sort(rng.choice(seq_len, size=rows_n, replace=False))
     t0 = time.perf_counter()
@@ -98,11 +102,22 @@ def cpu_baseline(bits, wl, n_video, seq_len, rows_n: int):
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "host_cores": nproc,
         "kind": "oracle",
         "sample": (f"{rows_n} random query rows x {HEADS} heads x batch {wl.batch} against all "
-                   f"{max(lk)} keys of {wl.name}, incl. fp64 RoPE of all K; {dt:.1f} s"),
+                   f"{max(lk)} keys of {wl.name}, incl. fp64 RoPE of all K; {dt:.1f} s; "
+                   f"'cores' = the BLAS threads its matrix products ran on (its elementwise "
+                   f"steps run on one), of the {nproc} host cores this process may use"),
         "seconds": dt,
     }
+
+
+def host_cores() -> int:
+    """Host cores this process may run on (nproc)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
 
 
 def timed(torch, stream, fn, reps: int) -> float:
@@ -281,7 +296,13 @@ def main() -> int:
     def to_dev(x):
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
 
+    inputs_sha = hvinputs.sha256_of((bits["q"], bits["k"], bits["v"]))
     q, k, v = to_dev(bits["q"]), to_dev(bits["k"]), to_dev(bits["v"])
+    # one unrotated copy of q and k per step (RoPE rotates in place)
+    n_copies = args.warmup + args.steps
+    qs = [q] + [q.clone() for _ in range(n_copies - 1)]
+    ks = [k] + [k.clone() for _ in range(n_copies - 1)]
+    progress(f"{n_copies} copies of q and k staged in HBM")
     out = torch.empty_like(q)
     # the forward's packed-V workspace, allocated once like the tensors
     ws = torch.empty(hv.hv_attention_workspace_bytes(wl.batch * L, wl.batch), dtype=torch.uint8,
@@ -289,19 +310,19 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev=None):
+    def step(i, ev=None):
         g = hv.hv_token_grid(wl.frames, wl.height, wl.width)
         if ev is not None:
             ev[0].record(stream)
-        hv.hv_rope3d_apply(q, k, g, wl.theta)
+        hv.hv_rope3d_apply(qs[i], ks[i], g, wl.theta)
         if ev is not None:
             ev[1].record(stream)
-        hv.hv_joint_attention_fwd(q, k, v, list(wl.valid), g.n_video, out=out, workspace=ws)
+        hv.hv_joint_attention_fwd(qs[i], ks[i], v, list(wl.valid), g.n_video, out=out, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     progress(f"warmup {args.warmup} done")
 
@@ -309,12 +330,18 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     rope_ms = [e[0].elapsed_time(e[1]) for e in events]
     attn_ms = [e[1].elapsed_time(e[2]) for e in events]
     progress(f"timed {args.steps} steps in {wall:.2f} s")
+    # every timed call saw the same rotated inputs
+    for i in range(1, args.steps):
+        assert torch.equal(qs[args.warmup], qs[args.warmup + i])
+    q, k = qs[-1], ks[-1]
+    del qs[:-1], ks[:-1]
+    torch.cuda.empty_cache()
 
     # The QK-norm + RoPE prologue (an alternative to the RoPE step that also
     # normalises every row): timed on its own, on the same resident q and k.
@@ -378,6 +405,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "inputs_sha256": inputs_sha,
+        "host_cores": host_cores(),
         "config": {"workload": name, "batch": wl.batch, "seq_len": L, "n_video": grid.n_video,
                    "text_valid": list(wl.valid), "heads": HEADS, "head_dim": HEAD_DIM,
                    "theta": wl.theta, "frames_hw": [wl.frames, wl.height, wl.width]},
