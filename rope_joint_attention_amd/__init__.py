@@ -48,7 +48,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, "lib", "libhvattn.so")
+    """Path of the library to load: $HVATTN_LIBRARY when set (another build
+    of the same sources, e.g. the host-sanitizer build), else the in-tree
+    lib/libhvattn.so."""
+    return os.environ.get("HVATTN_LIBRARY") or os.path.join(_PKG, "lib", "libhvattn.so")
 
 
 class HvError(RuntimeError):

@@ -1,9 +1,17 @@
 """Build libhvattn.so in-tree with hipcc for gfx950.
 
-    python -m rope_joint_attention_amd.build
+    python -m rope_joint_attention_amd.build               # lib/libhvattn.so
+    python -m rope_joint_attention_amd.build --host-sanitizers OUT.so
 
 Compiles every HIP source under csrc/ into one shared library next to this
 file (``lib/libhvattn.so``).  Always recompiles.
+
+--host-sanitizers builds the same sources with AddressSanitizer and
+UndefinedBehaviorSanitizer on the host code only (argument validation, launch
+set-up); the device code is compiled exactly as in the normal build.  The
+result needs the sanitizer runtime preloaded into the process
+(LD_PRELOAD=<ROCm llvm>/lib/clang/<v>/lib/linux/libclang_rt.asan-x86_64.so)
+and is selected for the Python binding with HVATTN_LIBRARY=OUT.so.
 """
 from __future__ import annotations
 
@@ -37,6 +45,20 @@ HIPCC_FLAGS = [
 ]
 
 
+# host-only instrumentation: every sanitizer flag applies to the host pass
+HOST_SANITIZER_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                        "-Xarch_host -fno-sanitize-recover=undefined "
+                        "-Xarch_host -fno-omit-frame-pointer -Xarch_host -g").split()
+
+
+def asan_runtime() -> str:
+    """The shared AddressSanitizer runtime of the ROCm clang (for LD_PRELOAD)."""
+    pats = glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+    if not pats:
+        raise RuntimeError("ROCm clang's AddressSanitizer runtime not found")
+    return sorted(pats)[-1]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -44,11 +66,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (needs ROCm)")
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(LIBDIR, exist_ok=True)
+def build(verbose: bool = True, out: str = LIB, host_sanitizers: bool = False) -> str:
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    tmp = out + ".tmp"
+    extra = HOST_SANITIZER_FLAGS if host_sanitizers else []
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -59,9 +82,12 @@ def build(verbose: bool = True) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build())
+    if len(sys.argv) == 3 and sys.argv[1] == "--host-sanitizers":
+        print(build(out=os.path.abspath(sys.argv[2]), host_sanitizers=True))
+    else:
+        print(build())
