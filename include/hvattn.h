@@ -39,10 +39,12 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
  *     and the call returns without synchronising.  Faults inside a kernel
  *     surface at the caller's next synchronisation.
- *   - The library allocates no memory and keeps no mutable global state;
- *     calls are thread-safe.  Scratch memory comes in as workspace
- *     arguments (the forward calls' packed V, the backward's D).  Calls that write overlapping memory on
- *     different streams race, as with any kernel.
+ *   - The library allocates no memory; calls are thread-safe.  Scratch
+ *     memory comes in as workspace arguments (the forward calls' packed V,
+ *     the backward's D), except in hv_joint_attention_bwd_noalloc, whose
+ *     scratch is a static device array (the only state the library keeps:
+ *     that array and its per-device addresses).  Calls that write
+ *     overlapping memory on different streams race, as with any kernel.
  *   - No C++ exception crosses this interface.
  */
 #ifndef HVATTN_H
@@ -61,6 +63,8 @@ extern "C" {
 #define HV_MAX_TOKEN_STRIDE (1 << 24) /* elements between consecutive tokens */
 #define HV_MAX_SEGMENTS 64    /* packed segments per varlen call */
 #define HV_MAX_MERGE_PARTS 16 /* partial results per merge call */
+/* device scratch of hv_joint_attention_bwd_noalloc: 32 MiB + 256 bytes per GPU */
+#define HV_NOALLOC_BWD_SCRATCH_BYTES ((32 << 20) + 256)
 
 typedef uint16_t hv_bf16; /* raw bfloat16 bits */
 
@@ -290,6 +294,35 @@ int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                            const int32_t* text_valid_len, int64_t n_video,
                            hv_bf16* dq, hv_bf16* dk, hv_bf16* dv, float* delta,
                            const hv_layout* layout, float softmax_scale, void* stream);
+
+/* hv_joint_attention_bwd_noalloc: hv_joint_attention_bwd for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * training or serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments and results, but the delta workspace lives in a
+ * static device array of the library, HV_NOALLOC_BWD_SCRATCH_BYTES on every
+ * GPU it runs on (taken when the library's code is loaded onto the GPU and
+ * held until the process ends).  The call allocates nothing; its first call
+ * on a device looks up that device's copy (hipGetSymbolAddress, with the
+ * device current) and keeps the address.
+ *   arguments   as hv_joint_attention_bwd, without delta; the current HIP
+ *               device must be the one that holds the tensors and runs
+ *               `stream`
+ *   size limit  2 * batch * 24 * seq_len * 4 + 256 bytes must fit the
+ *               scratch, i.e. batch * seq_len <= 174762 (720x1280x129 at
+ *               batch 1 is 119056); larger calls return HV_ERR_UNSUPPORTED
+ *               without launching
+ * Every call on one GPU uses that GPU's one scratch array, which keeps what
+ * the last call left there (the kernels rewrite everything they read first):
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and must be ordered by the caller.
+ * Errors: as hv_joint_attention_bwd; HV_ERR_UNSUPPORTED also for calls over
+ * the size limit or a device index >= 64; HV_ERR_HIP when the scratch
+ * address cannot be found. */
+int hv_joint_attention_bwd_noalloc(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                                   const hv_bf16* out, const hv_bf16* dout, const float* lse,
+                                   const int32_t* text_valid_len, int64_t n_video,
+                                   hv_bf16* dq, hv_bf16* dk, hv_bf16* dv,
+                                   const hv_layout* layout, float softmax_scale, void* stream);
 
 /* hv_joint_attention_varlen_bwd: gradients of hv_joint_attention_varlen_fwd
  * (packed segments; notes page section 9.1 for the packed form, the report

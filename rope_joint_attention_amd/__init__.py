@@ -19,6 +19,8 @@ not built, every call raises (there is no fallback).
                                   ...) -> (out, lse)
     hv_joint_attention_bwd(q, k, v, out, dout, lse, text_valid_len, n_video,
                            ...) -> (dq, dk, dv)
+    hv_joint_attention_bwd_noalloc(q, k, v, out, dout, lse, text_valid_len,
+                                   n_video, dq, dk, dv) -> (dq, dk, dv)
     hv_joint_attention_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q,
                                   cu_seqlens_k=None, ...) -> (dq, dk, dv)
 """
@@ -33,7 +35,7 @@ __all__ = [
     "hv_token_grid", "hv_rope3d_apply", "hv_qk_norm_rope3d_apply", "hv_attention_workspace_bytes",
     "hv_joint_attention_fwd",
     "hv_attention_fwd_lse", "hv_attention_merge", "hv_joint_attention_varlen_fwd",
-    "hv_joint_attention_bwd", "hv_joint_attention_varlen_bwd",
+    "hv_joint_attention_bwd", "hv_joint_attention_bwd_noalloc", "hv_joint_attention_varlen_bwd",
     "hv_status_string", "library_path", "load_library",
 ]
 
@@ -42,6 +44,7 @@ HV_HEAD_DIM = 128
 HV_MAX_BATCH = 64
 HV_MAX_SEGMENTS = 64
 HV_MAX_MERGE_PARTS = 16
+HV_NOALLOC_BWD_SCRATCH_BYTES = (32 << 20) + 256
 HV_OK, HV_ERR_INVALID_ARG, HV_ERR_UNSUPPORTED, HV_ERR_HIP = 0, -1, -2, -3
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -143,6 +146,10 @@ def load_library():
         ctypes.POINTER(ctypes.c_int32), ctypes.c_int64] + [ctypes.c_void_p] * 4 + [
         ctypes.POINTER(_Layout), ctypes.c_float, ctypes.c_void_p]
     lib.hv_joint_attention_bwd.restype = ctypes.c_int
+    lib.hv_joint_attention_bwd_noalloc.argtypes = [ctypes.c_void_p] * 6 + [
+        ctypes.POINTER(ctypes.c_int32), ctypes.c_int64] + [ctypes.c_void_p] * 3 + [
+        ctypes.POINTER(_Layout), ctypes.c_float, ctypes.c_void_p]
+    lib.hv_joint_attention_bwd_noalloc.restype = ctypes.c_int
     lib.hv_joint_attention_varlen_bwd.argtypes = [ctypes.c_void_p] * 6 + [
         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32] + [
         ctypes.c_void_p] * 4 + [ctypes.POINTER(_Layout), ctypes.c_float, ctypes.c_void_p]
@@ -481,6 +488,38 @@ def hv_joint_attention_bwd(q, k, v, out, dout, lse, text_valid_len: Optional[Seq
     if st != HV_OK:
         raise HvError(st, "hv_joint_attention_bwd")
     return tuple(grads)
+
+
+def hv_joint_attention_bwd_noalloc(q, k, v, out, dout, lse, text_valid_len: Optional[Sequence[int]],
+                                   n_video: int, dq, dk, dv, softmax_scale: Optional[float] = None):
+    """hv_joint_attention_bwd with the library's static device scratch in place
+    of the delta workspace (see hvattn.h): for callers that cannot allocate.
+    dq, dk, dv are required (this wrapper allocates nothing either).
+    Returns (dq, dk, dv)."""
+    lay = _layout_of(q, "q")
+    for t, name in ((k, "k"), (v, "v"), (out, "out"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                    (dv, "dv")):
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if not _same_layout(lay, _layout_of(t, name)):
+            raise ValueError(f"q and {name} must share shape and strides")
+    if lse is None:
+        raise ValueError("lse (the forward's log-sum-exp) is required")
+    _lse_buffer(lse, (q.shape[0], HV_HEADS, q.shape[1]), q.device, "lse")
+    valid_arr = None
+    if text_valid_len is not None:
+        vals = [int(x) for x in text_valid_len]
+        if len(vals) != q.shape[0]:
+            raise ValueError("text_valid_len needs one entry per batch element")
+        valid_arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = load_library().hv_joint_attention_bwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        valid_arr, int(n_video), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ctypes.byref(lay),
+        scale, _stream_of(q))
+    if st != HV_OK:
+        raise HvError(st, "hv_joint_attention_bwd_noalloc")
+    return dq, dk, dv
 
 
 def hv_joint_attention_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q: Sequence[int],

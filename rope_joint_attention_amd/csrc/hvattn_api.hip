@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hv_internal.h"
 
 namespace {
@@ -94,9 +96,11 @@ float scale_log2(float softmax_scale) {
 // Pointers, alignment and overlap of the backward's arguments (shared by the
 // padded and the packed forms).  lse holds batch * 24 * seq_len floats; delta
 // twice as many, followed by 256 bytes of work counters.
+// A NULL delta is accepted only with own_delta == false (the allocation-free
+// form, whose delta is the library's static scratch and meets no argument).
 int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, const hv_bf16* out,
                       const hv_bf16* dout, const float* lse, hv_bf16* dq, hv_bf16* dk, hv_bf16* dv,
-                      float* delta, const hv_layout* layout) {
+                      float* delta, const hv_layout* layout, bool own_delta = true) {
   int64_t extent = 0;
   int st = check_layout(layout, &extent);
   if (st != HV_OK) return st;
@@ -106,8 +110,8 @@ int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, cons
     if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
   for (const hv_bf16* t : outs)
     if (!t || !aligned16(t)) return HV_ERR_INVALID_ARG;
-  if (!lse || !delta || ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)delta & 3u) != 0)
-    return HV_ERR_INVALID_ARG;
+  if (!lse || ((uintptr_t)lse & 3u) != 0) return HV_ERR_INVALID_ARG;
+  if (own_delta && (!delta || ((uintptr_t)delta & 3u) != 0)) return HV_ERR_INVALID_ARG;
   for (int i = 0; i < 3; ++i) {
     for (const hv_bf16* t : ins)
       if (overlap(outs[i], t, layout, extent)) return HV_ERR_INVALID_ARG;
@@ -115,7 +119,9 @@ int check_bwd_buffers(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v, cons
       if (overlap(outs[i], outs[j], layout, extent)) return HV_ERR_INVALID_ARG;
   }
   const uintptr_t vb = (uintptr_t)layout->batch * HV_HEADS * layout->seq_len * sizeof(float);
-  const uintptr_t db = 2 * vb + hv::kCounterBytes;  // -D, -lse/scale, the two work counters
+  // -D, -lse/scale, the two work counters (none of the caller's when the
+  // library's scratch holds them)
+  const uintptr_t db = own_delta ? 2 * vb + hv::kCounterBytes : 0;
   const uintptr_t tb = (uintptr_t)extent * sizeof(hv_bf16);
   if (ranges_meet(delta, db, lse, vb)) return HV_ERR_INVALID_ARG;
   for (const hv_bf16* t : ins)
@@ -167,6 +173,57 @@ void rope_frequencies(float theta, float* freq) {
   for (int a = 0; a < 3; ++a)
     for (int j = 0; j < widths[a] / 2; ++j)
       freq[pair++] = (float)pow((double)theta, -2.0 * j / widths[a]);
+}
+
+// Segment table of the padded batch for the backward: entry b's queries
+// attend to its first n_video + text_valid_len[b] keys.
+int padded_bwd_segments(hv::BwdParams& p, const int32_t* text_valid_len, int64_t n_video,
+                        const hv_layout* layout) {
+  if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
+  memset(&p, 0, sizeof(p));
+  const int64_t text_cap = layout->seq_len - n_video;
+  const int L = layout->seq_len;
+  for (int b = 0; b < layout->batch; ++b) {
+    const int64_t valid = text_valid_len ? text_valid_len[b] : text_cap;
+    if (valid < 0 || valid > text_cap) return HV_ERR_INVALID_ARG;
+    if (n_video + valid < 1) return HV_ERR_INVALID_ARG;
+    hv::BwdSegment& sg = p.seg[b];
+    sg.q_off = sg.k_off = (int64_t)b * layout->stride_b;
+    sg.v_off = (int64_t)b * HV_HEADS * L;
+    sg.q_len = sg.k_rows = L;
+    sg.k_len = (int32_t)(n_video + valid);
+  }
+  p.n_seg = layout->batch;
+  return HV_OK;
+}
+
+// Scratch of hv_joint_attention_bwd_noalloc: what the delta workspace of
+// hv_joint_attention_bwd holds (-D, -lse/scale, the two work counters), in a
+// fixed array of device memory.  Every GPU the library runs on has its own
+// copy at its own address, kept until the process ends; in host code the
+// array's name is not a device address, so it is only reached through the
+// per-device addresses below.
+static __device__ __align__(256) unsigned char scratch[HV_NOALLOC_BWD_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch on the current device, looked up once per
+// device (with that device current) and kept.
+int bwd_scratch_of_current_device(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return HV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return HV_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return HV_OK;
 }
 
 }  // namespace
@@ -469,25 +526,39 @@ int hv_joint_attention_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
                            float softmax_scale, void* stream) {
   int st = check_bwd_buffers(q, k, v, out, dout, lse, dq, dk, dv, delta, layout);
   if (st != HV_OK) return st;
-  if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
-  if (layout->batch == 0 || layout->seq_len == 0) return HV_OK;
-
-  hv::BwdParams p;
-  memset(&p, 0, sizeof(p));
-  const int64_t text_cap = layout->seq_len - n_video;
-  const int L = layout->seq_len;
-  for (int b = 0; b < layout->batch; ++b) {
-    const int64_t valid = text_valid_len ? text_valid_len[b] : text_cap;
-    if (valid < 0 || valid > text_cap) return HV_ERR_INVALID_ARG;
-    if (n_video + valid < 1) return HV_ERR_INVALID_ARG;
-    hv::BwdSegment& sg = p.seg[b];
-    sg.q_off = sg.k_off = (int64_t)b * layout->stride_b;
-    sg.v_off = (int64_t)b * HV_HEADS * L;
-    sg.q_len = sg.k_rows = L;
-    sg.k_len = (int32_t)(n_video + valid);
+  if (layout->batch == 0 || layout->seq_len == 0) {
+    if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
+    return HV_OK;
   }
-  p.n_seg = layout->batch;
+  hv::BwdParams p;
+  st = padded_bwd_segments(p, text_valid_len, n_video, layout);
+  if (st != HV_OK) return st;
   return launch_bwd(p, q, k, v, out, dout, lse, dq, dk, dv, delta, layout, softmax_scale, stream);
+}
+
+int hv_joint_attention_bwd_noalloc(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
+                                   const hv_bf16* out, const hv_bf16* dout, const float* lse,
+                                   const int32_t* text_valid_len, int64_t n_video, hv_bf16* dq,
+                                   hv_bf16* dk, hv_bf16* dv, const hv_layout* layout,
+                                   float softmax_scale, void* stream) {
+  int st = check_bwd_buffers(q, k, v, out, dout, lse, dq, dk, dv, nullptr, layout, false);
+  if (st != HV_OK) return st;
+  if (layout->batch == 0 || layout->seq_len == 0) {
+    if (n_video < 0 || n_video > layout->seq_len) return HV_ERR_INVALID_ARG;
+    return HV_OK;
+  }
+  hv::BwdParams p;
+  st = padded_bwd_segments(p, text_valid_len, n_video, layout);
+  if (st != HV_OK) return st;
+  // -D and -lse/scale for every (batch, head, row), then the counters
+  const int64_t need = 2 * (int64_t)layout->batch * HV_HEADS * layout->seq_len * (int64_t)sizeof(float) +
+                       hv::kCounterBytes;
+  if (need > HV_NOALLOC_BWD_SCRATCH_BYTES) return HV_ERR_UNSUPPORTED;
+  float* scratch_ptr = nullptr;
+  st = bwd_scratch_of_current_device(&scratch_ptr);
+  if (st != HV_OK) return st;
+  return launch_bwd(p, q, k, v, out, dout, lse, dq, dk, dv, scratch_ptr, layout, softmax_scale,
+                    stream);
 }
 
 int hv_joint_attention_varlen_bwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,

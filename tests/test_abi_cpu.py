@@ -400,6 +400,45 @@ def test_backward_empty_call():
     assert bwd(lay=layout(batch=0), valid=None, n_video=0) == hv.HV_OK
 
 
+def bwd_noalloc(q=FAKE, k=FAKE + SEP, v=FAKE + 2 * SEP, o=FAKE + 3 * SEP, g=FAKE + 4 * SEP, lse=LSE,
+                valid=(10,), n_video=40, dq=FAKE + 10 * SEP, dk=FAKE + 11 * SEP, dv=FAKE + 12 * SEP,
+                lay=None):
+    lib = hv.load_library()
+    lay = layout() if lay is None else lay
+    arr = None if valid is None else (ctypes.c_int32 * max(1, len(valid)))(*valid)
+    return lib.hv_joint_attention_bwd_noalloc(q, k, v, o, g, lse, arr, n_video, dq, dk, dv,
+                                              ctypes.byref(lay) if lay is not False else None,
+                                              0.0, None)
+
+
+NOALLOC_ROWS = (hv.HV_NOALLOC_BWD_SCRATCH_BYTES - 256) // (2 * 24 * 4)   # batch * seq_len limit
+
+
+@pytest.mark.parametrize("kwargs,expect", [
+    (dict(q=0), E), (dict(k=0), E), (dict(v=0), E), (dict(o=0), E), (dict(g=0), E),
+    (dict(lse=0), E), (dict(dq=0), E), (dict(dk=0), E), (dict(dv=0), E),
+    (dict(lay=False), E), (dict(dq=FAKE + 10 * SEP + 2), E), (dict(lse=LSE + 1), E),
+    (dict(dq=FAKE + 100 * 3072 * 2), E),                  # dq inside q
+    (dict(dv=FAKE + 4 * SEP), E),                         # dv is dout
+    (dict(lse=FAKE + 2 * SEP + 256), E),                  # lse inside v
+    (dict(valid=(-1,)), E), (dict(valid=(261,)), E), (dict(n_video=0, valid=(0,)), E),
+    (dict(n_video=301), E),
+    (dict(lay=layout(heads=8)), U), (dict(lay=layout(batch=65), valid=None), U),
+    # over the static scratch: one row more than it holds, in one or two entries
+    (dict(lay=layout(seq=NOALLOC_ROWS + 1), n_video=NOALLOC_ROWS + 1 - 256, valid=(256,)), U),
+    (dict(lay=layout(batch=2, seq=NOALLOC_ROWS // 2 + 1, sb=(NOALLOC_ROWS // 2 + 1) * 3072),
+          n_video=NOALLOC_ROWS // 2 + 1 - 256, valid=(256, 3)), U),
+])
+def test_backward_noalloc_validation(kwargs, expect):
+    assert bwd_noalloc(**kwargs) == expect
+
+
+def test_backward_noalloc_limit_and_empty_call():
+    assert NOALLOC_ROWS == 174762                          # 720x1280x129 (119056 rows) fits
+    assert bwd_noalloc(lay=layout(batch=0), valid=None, n_video=0) == hv.HV_OK
+    assert bwd_noalloc(lay=layout(batch=0), valid=None, n_video=301) == E
+
+
 def varlen_bwd(cq=(0, 100, 300), ck=None, n=None, lay=None, **kw):
     lib = hv.load_library()
     ck = cq if ck is None else ck
