@@ -132,6 +132,33 @@ def timed(torch, stream, fn, reps: int) -> float:
     return ev[0].elapsed_time(ev[1]) / reps
 
 
+def graph_timed(torch, fn, calls: int, reps: int) -> float:
+    """Average ms of one fn() call with `calls` calls captured in one HIP graph
+    and the graph replayed `reps` times: the GPU's time per call without the
+    host's per-call launch work (which sets the eager time of small calls)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / (reps * calls)
+    del g
+    return ms
+
+
 def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int) -> dict:
     """Measurements of the sequence-parallel and packed attention forms on the
     resident tensors (not part of the timed step).
@@ -145,7 +172,11 @@ def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int)
       tokens packed as [valid | padded tail] segments of one sequence (the
       padded tails attend to themselves), one hv_joint_attention_varlen_fwd.
     workloads: attention and RoPE of each of the five workloads (device-side
-      random inputs of the workload's shape, timing only).
+      random inputs of the workload's shape, timing only), each call with its
+      workspace allocated beforehand: `attn_ms` eager calls back to back,
+      `attn_ms_graph` calls replayed from a HIP graph (the GPU time per call
+      without the host's launch work, which dominates the eager time of the
+      smallest workload); the TFLOP/s and % of peak use the graph time.
     backward: hv_joint_attention_bwd at this size.  `tflops` counts the usual
       five matrix products of an attention backward (2.5x the forward's
       FLOPs); the kernels execute seven (S and dP are formed twice, once for
@@ -216,18 +247,25 @@ def extra_rows(hv, hvinputs, torch, np, q, k, v, wl, grid, L, stream, reps: int)
         qw, kw, vw = (torch.randn((w.batch, Lw, HEADS, HEAD_DIM), device=q.device, generator=gen)
                       .to(torch.bfloat16) for _ in range(3))
         ow = torch.empty_like(qw)
-        ms_a = timed(torch, stream, lambda: hv.hv_joint_attention_fwd(
-            qw, kw, vw, list(w.valid), gw.n_video, out=ow), reps)
+        wsw = torch.empty(hv.hv_attention_workspace_bytes(w.batch * Lw, w.batch), dtype=torch.uint8,
+                          device=q.device)
+
+        def call():
+            hv.hv_joint_attention_fwd(qw, kw, vw, list(w.valid), gw.n_video, out=ow, workspace=wsw)
+
+        ms_a = timed(torch, stream, call, reps)
+        small = w.batch * Lw <= 16384
+        ms_g = graph_timed(torch, call, 50 if small else 1, 4 if small else 2)
         ms_r = timed(torch, stream, lambda: hv.hv_rope3d_apply(qw, kw, gw, w.theta), reps)
         lkw = [gw.n_video + x for x in w.valid]
         flw = 4.0 * HEADS * HEAD_DIM * Lw * sum(lkw)
         rbytes = 4.0 * w.batch * gw.n_video * HEADS * HEAD_DIM * 2
-        wlt[name] = {"seq_len": Lw, "attn_ms": round(ms_a, 4),
-                     "attn_tflops": round(flw / (ms_a / 1e3) / 1e12, 2),
-                     "pct_mfma_peak": round(100.0 * flw / (ms_a / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        wlt[name] = {"seq_len": Lw, "attn_ms": round(ms_a, 4), "attn_ms_graph": round(ms_g, 4),
+                     "attn_tflops": round(flw / (ms_g / 1e3) / 1e12, 2),
+                     "pct_mfma_peak": round(100.0 * flw / (ms_g / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                      "rope_ms": round(ms_r, 4),
                      "rope_GBps": round(rbytes / (ms_r / 1e3) / 1e9, 1)}
-        del qw, kw, vw, ow
+        del qw, kw, vw, ow, wsw
     out["workloads"] = wlt
 
     # backward of the headline attention: forward with log-sum-exp once, then

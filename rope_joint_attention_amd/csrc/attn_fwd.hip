@@ -33,10 +33,14 @@
 //   S^T (64 keys x 32 queries) = K_tile * Q^T   -- lane l owns query l%32, so
 //       row statistics are 32 in-register values plus one exchange between
 //       the two 32-lane halves (v_permlane32_swap);
-//   online softmax in the log2 domain with exp2; the running reference m is
-//       only raised when a row maximum exceeds it by more than 8 (factor 256),
-//       which keeps every probability <= 256 and the result exact while
-//       skipping almost all accumulator rescales;
+//   online softmax in the log2 domain with exp2.  The reference m of a row
+//       is its maximum over the first tile; later tiles compute no maximum:
+//       the row's running sum of weights bounds every weight, and when it
+//       passes 2^40 the reference rises by 32 (the accumulators are scaled
+//       by 2^-32 exactly).  A block whose weights still overflow is redone
+//       with the reference following each tile's maximum (raised only when
+//       it exceeds the reference by more than 8, so weights stay <= 256);
+//       either way the result is exact;
 //   O^T (128 channels x 32 queries) += V^T_tile * P^T -- P^T stays in the
 //       registers the softmax produced (bf16).  The V^T operand wants 8 keys
 //       of one channel per lane.  With a workspace, V is first packed
@@ -143,12 +147,18 @@ __device__ __forceinline__ float tile_max(const f32x16& s0, const f32x16& s1, fl
   return max_across_halves(mx) * c2;
 }
 
+// Scores of keys >= lim (tile-relative) become -inf.  Register v of a lane
+// holds key 8(v/4) + 4hh + v%4; the lane-dependent part is moved to the
+// limit, so every compare is against an immediate (with the key index as the
+// loop-invariant operand the compiler keeps 32 key indices in registers for
+// the whole key loop).
 __device__ __forceinline__ void mask_tile(f32x16& s0, f32x16& s1, int lim, int hh) {
+  const int rel = lim - 4 * hh;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int key = 8 * (v >> 2) + 4 * hh + (v & 3);
-    if (key >= lim) s0[v] = -INFINITY;
-    if (key + 32 >= lim) s1[v] = -INFINITY;
+    const int key = 8 * (v >> 2) + (v & 3);
+    if (key >= rel) s0[v] = -INFINITY;
+    if (key + 32 >= rel) s1[v] = -INFINITY;
   }
 }
 
@@ -166,6 +176,23 @@ __device__ __forceinline__ void update_reference(float mx, float& m_run, float& 
       for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
     l_run *= alpha;
     m_run = m_new;
+  }
+}
+
+// Without per-tile maxima: the sum of a row's weights bounds each of them,
+// so when it passes 2^40 the reference rises by 32 and the accumulators are
+// scaled by 2^-32 (exactly).  The two lanes of a row decide on their joint
+// sum, so they keep one reference.
+__device__ __forceinline__ void bound_weights(float& m_run, float& l_run, f32x16 (&o)[4]) {
+  const bool need = sum_across_halves(l_run) > 0x1p40f;
+  if (__any(need)) {
+    const float alpha = need ? 0x1p-32f : 1.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
+    l_run *= alpha;
+    if (need) m_run += 32.0f;
   }
 }
 
@@ -366,12 +393,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   };
 
   f32x16 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
-  float m_run = -INFINITY;  // running reference, log2 domain
-  float l_run = 0.f;        // this lane's share of the denominator (bf16-rounded weights)
+  float m_run;  // reference, log2 domain
+  float l_run;  // this lane's share of the denominator (bf16-rounded weights)
   const float c2 = p.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const f32x16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -399,6 +422,28 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     const u32x4 v = {w[0], w[1], w[2], w[3]};
     return __builtin_bit_cast(bf16x8, v);
   };
+
+  // The block's computation, in one of two modes.
+  //   kTrack = false (every block starts here): the reference m starts at
+  //     the row maximum of tile 0; no later tile's maximum is computed.
+  //     Instead the row's sum of weights, which bounds each weight, is kept
+  //     below 2^40 by raising m in steps of 32 (bound_weights): one compare
+  //     per step instead of a 32-value maximum.  The weights stay finite
+  //     unless a tile's scores jump far (over 2^80) above everything before
+  //     them, and the result is exact either way (every weight of a row
+  //     carries the row's reference, which cancels in O / l).
+  //   kTrack = true: the reference follows the row maximum tile by tile
+  //     (raised lazily, see update_reference), so every weight is <= 2^8.
+  //     A block whose sum of weights is not below 2^64 (or not finite) after
+  //     the fast mode is run again in this mode.
+  auto run = [&](auto track) __attribute__((always_inline)) {
+  constexpr bool kTrack = decltype(track)::value;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+  m_run = -INFINITY;
+  l_run = 0.f;
 
   // ---- prologue: K tiles 0..3 and V tiles 0..2 requested; scores of tile 0
   load_k(I0{}, 0);
@@ -513,7 +558,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
         kf[2] = k_frag(KN{}, 0, 1);
         kf[3] = k_frag(KN{}, 1, 1);
       }
-      if (i >= 8) {  // row maximum of tile t+1, in eight pieces of one chain
+      if (kTrack && i >= 8) {  // row maximum of tile t+1, in eight pieces of one chain
         const int j = i - 8;
         const f32x16& sv = nxt[j >> 2];
         const int b = 4 * (j & 3);
@@ -523,7 +568,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    const float mx = max_across_halves(part_run) * c2;
+    const float mx = kTrack ? max_across_halves(part_run) * c2 : 0.f;
     __builtin_amdgcn_sched_barrier(0);
     // chunk 0 of tile t+2 (after the last step: a tile that is never used)
     cur[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], zero16, 0, 0, 0);
@@ -534,7 +579,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     // the 4 loads just issued stay in flight, and so may the two reads of K
     // tile t+2 (its stage is not refilled before the next barrier)
     barrier_after<4, 2>();
-    update_reference(mx, m_run, l_run, o);
+    if constexpr (kTrack) update_reference(mx, m_run, l_run, o);
+    else bound_weights(m_run, l_run, o);
   };
 
   const int last = ntiles - 1;  // steps run for t = 0 .. last-1
@@ -577,13 +623,21 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
       default: final_pv(I3{}); break;
     }
   }
-  // no LDS access follows; drain the remaining (dead) tile loads before exit
+  // no LDS access follows; drain the remaining (dead) tile loads
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  };  // run
+
+  run(std::false_type{});
+  float l_tot = sum_across_halves(l_run);
+  // every wave of the block joins (the waves share the K/V tiles in LDS)
+  if (__syncthreads_or(!(l_tot < 0x1p64f))) {
+    run(std::true_type{});
+    l_tot = sum_across_halves(l_run);
+  }
 
   // ---- epilogue: O / l, round to bf16, store rows that exist; optionally
   // the natural-log log-sum-exp of the row's logits: the weights summed in l
   // are 2^(s*c2 - m), so sum_j e^(scale*s_j) = 2^m * l.
-  const float l_tot = sum_across_halves(l_run);
   const float inv = 1.0f / l_tot;
   const int orow = q0 + l32;
   if (orow < L) {

@@ -88,6 +88,48 @@ def test_attention_peaky_softmax(q_scale):
     log(f"  peaky x{q_scale}: {e}")
 
 
+def _directed_inputs(L, seed, key_boost):
+    """q rows near 10 u for a fixed unit vector u, k rows with key_boost[j] u
+    added: scores grow (or jump) along the sequence as key_boost says."""
+    r = np.random.default_rng(seed)
+    u = r.standard_normal(128)
+    u /= np.linalg.norm(u)
+    q = 0.3 * r.standard_normal((1, L, 24, 128)) + 10.0 * u
+    k = r.standard_normal((1, L, 24, 128)) + key_boost[None, :, None, None] * u
+    v = r.standard_normal((1, L, 24, 128))
+    return {n: hvinputs.f32_to_bf16_bits(x.astype(np.float32)) for n, x in (("q", q), ("k", k), ("v", v))}
+
+
+@pytest.mark.parametrize("case", ["rising", "late_jump"])
+def test_attention_weight_bounds(case):
+    """Scores that rise along the sequence by ~80 (log2 units): the sum of
+    weights passes 2^40 and the reference moves up in steps of 32; and scores
+    that jump by ~150 in a late tile, past the fp32 range of the first
+    tile's reference, so the block is redone with per-tile maxima.  Both
+    paths (packed V and V in place) must agree bit for bit and match the
+    oracle."""
+    import torch
+    import rope_joint_attention_amd as hv
+
+    n_video, cap, valid = 2300, 20, [20]
+    L = n_video + cap
+    boost = np.zeros(L)
+    if case == "rising":
+        boost[:] = np.linspace(0.0, 60.0, L)
+    else:
+        boost[2200:2240] = 110.0
+    bits = _directed_inputs(L, 99, boost)
+    q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
+    a = hv.hv_joint_attention_fwd(q, k, v, valid, n_video)
+    b = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, pack_v=False)
+    torch.cuda.synchronize()
+    a, b = torch_to_bits(a), torch_to_bits(b)
+    assert np.array_equal(a, b)
+    ref = joint_attention(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), n_video, valid)
+    e = assert_close(widen(a), ref, case)
+    log(f"  {case}: {e}")
+
+
 def test_attention_identical_keys_give_mean_of_v():
     B, n_video, cap, valid = 1, 700, 60, [33]
     L = n_video + cap

@@ -5,6 +5,8 @@ hv_joint_attention_varlen_fwd first rewrite V tile by tile channel-major into
 it and read each P V operand with one 16-byte LDS read; without one they read
 V in place with the transposing LDS read.  Both feed the same values into the
 same MFMA slots, so the outputs (and log-sum-exps) must agree bit for bit.
+(Small padded calls given room for it take the key-range split instead; the
+tests here size the workspace for packing alone where they compare paths.)
 
 * bitwise agreement of the two paths on small shapes around the 64-key tile
   (ragged tails, one key, exact multiples of 64, batch entries with different
@@ -66,6 +68,15 @@ SHAPES = [
 ]
 
 
+def packed_workspace(n_video, valid):
+    """A workspace of exactly the packed-V size: enough for the packed path,
+    too small for the key-range split of small calls, so the call packs V."""
+    import torch
+
+    need = sum((n_video + x + 63) // 64 for x in valid) * 24 * TILE * 2 + 256
+    return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
 @pytest.mark.parametrize("B,n_video,cap,valid", SHAPES, ids=lambda x: str(x))
 def test_packed_and_inplace_paths_agree_bitwise(B, n_video, cap, valid):
     import torch
@@ -75,7 +86,7 @@ def test_packed_and_inplace_paths_agree_bitwise(B, n_video, cap, valid):
     bits = hvinputs.draw_qkv(B, L, seed=31 * L + B)
     q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
     log(f"packed vs in-place B={B} N={n_video} L={L} valid={valid}")
-    a = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, pack_v=True)
+    a = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, workspace=packed_workspace(n_video, valid))
     b = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, pack_v=False)
     torch.cuda.synchronize()
     assert np.array_equal(torch_to_bits(a), torch_to_bits(b))
@@ -131,6 +142,9 @@ def test_workspace_holds_the_packed_layout():
     need = sum((n_video + x + 63) // 64 for x in valid) * 24 * TILE * 2 + 256
     cap_bytes = hv.hv_attention_workspace_bytes(B * L, B)
     assert cap_bytes >= need
+    # 1 KB more than the packed layout needs: too little for the key-range
+    # split this small call would otherwise take, so V is packed
+    cap_bytes = need + 1024
     ws = torch.full((cap_bytes // 2,), 0x1234, dtype=torch.int16, device="cuda")
     log(f"packed layout B={B} L={L} valid={valid}: need {need} bytes of {cap_bytes}")
     out = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, workspace=ws)
@@ -169,19 +183,27 @@ def test_varlen_workspace_layout_skips_segments_without_queries():
 
 
 def test_workspace_reused_by_consecutive_calls():
+    # the second (smaller) call finds the first one's packed tiles and counter
+    # in the workspace and must not depend on them: it matches the same call
+    # on a fresh NaN-filled workspace bit for bit.  The first call packs V;
+    # the second is small enough to be split over its keys.
     import torch
     import rope_joint_attention_amd as hv
 
-    ws = torch.empty(hv.hv_attention_workspace_bytes(1300, 1), dtype=torch.uint8, device="cuda")
+    nbytes = max(hv.hv_attention_workspace_bytes(1300, 1), hv.hv_attention_workspace_bytes(333, 1))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     for L, valid, seed in ((1300, [100], 96), (333, [17], 97)):
         bits = hvinputs.draw_qkv(1, L, seed=seed)
         q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
         n_video = L - 120
         log(f"workspace reuse L={L}")
         a = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, workspace=ws)
-        b = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, pack_v=False)
+        fresh = torch.full((nbytes // 2,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        b = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, workspace=fresh)
         torch.cuda.synchronize()
         assert np.array_equal(torch_to_bits(a), torch_to_bits(b))
+        ref = joint_attention(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), n_video, valid)
+        assert_close(widen(torch_to_bits(a)), ref, f"reused workspace L={L}")
 
 
 def test_too_small_workspace_is_refused():
