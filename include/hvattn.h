@@ -157,20 +157,13 @@ int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
  * largest sizes; both give bitwise identical results.  A call
  * needs, over its segments with query rows (a batch entry of the padded
  * forms, a packed clip), sum ceil(keys / 64) * 64 * 24 * 128 * 2 bytes plus
- * 256 bytes (none when no segment has query rows).
- * Small padded calls: an hv_joint_attention_fwd call with at most 128 query
- * blocks (24 * batch * ceil(seq_len / 256) <= 128) whose every batch entry
- * has at least two 64-key tiles, given a workspace of at least
- * parts * batch * seq_len * (24 * 128 * 2 + 24 * 4) bytes, is split over
- * its keys instead of packing V: each entry's keys are cut into `parts`
- * (2..8) runs of whole tiles, the runs are computed by one launch into
- * partial outputs and log-sum-exps in the workspace, and a second kernel
- * merges them exactly (as hv_attention_merge does), so that more CUs share
- * the call.  The result then agrees with the unsplit call within bf16
- * rounding of the partial results rather than bit for bit.
+ * 256 bytes (none when no segment has query rows).  A call whose query
+ * blocks (24 heads x ceil(rows / 256) per segment) all fit in one round of
+ * workgroups (at most one per compute unit) reads V in place even with a
+ * workspace: there is nothing to share out, and packing would cost one more
+ * launch and pass over V; the results are the same bit for bit.
  * hv_attention_workspace_bytes(n_keys, n_segments) returns an upper bound
- * for n_keys keys in all over n_segments segments (covering the split when
- * n_keys <= 1280):
+ * for n_keys keys in all over n_segments segments:
  *   hv_joint_attention_fwd         n_keys = batch * seq_len, n_segments = batch
  *   hv_attention_fwd_lse           n_keys = batch * kv seq_len, n_segments = batch
  *   hv_joint_attention_varlen_fwd  n_keys = T, n_segments as passed

@@ -453,7 +453,11 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   load_v(I0{}, 0);
   load_v(I1{}, min(1, ntiles - 1));
   load_v(I2{}, min(2, ntiles - 1));
-  barrier_after<0>();
+  // Each wave's loads complete in the order issued: its eight Q loads, then
+  // two instructions per tile, K 0..3 and V 0..2.  Tile 0's scores wait only
+  // for Q and K tile 0 (12 instructions may still be in flight), so the first
+  // MFMAs start one tile's latency after the block begins instead of seven.
+  barrier_after<12>();
   f32x16 sa[2], sb[2];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
@@ -462,6 +466,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   }
   if (ntiles == 1) mask_tile(sa[0], sa[1], Lk, hh);
   update_reference(tile_max(sa[0], sa[1], c2), m_run, l_run, o);
+  barrier_after<10>();  // K tile 1 in place
   // K operands of the first step (tile 1) are read, and its first two QK^T
   // MFMAs issued, before its barrier (see the end of a step)
   bf16x8 kf[4];
@@ -473,7 +478,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   sb[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[1], qf[0], zero16, 0, 0, 0);
   kf[0] = k_frag(I1{}, 0, 2);
   kf[1] = k_frag(I1{}, 1, 2);
-  barrier_after<0>();  // every wave has read K tile 0 before its buffer is refilled
+  // K tiles 2, 3 and V tile 0 in place for the first step (V tiles 1 and 2 may
+  // still be in flight: the first step's barrier waits for them), and every
+  // wave has read K tile 0 before its buffer is refilled
+  barrier_after<4>();
 
   // ---- steady state.  Step t (tile t+1 exists; U = t % 4 at compile time),
   // in fixed instruction order (sched_barrier fences between bundles keep the
@@ -691,17 +699,25 @@ hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream) {
   }
   p.n_blocks = blocks;
   if (blocks == 0) return hipSuccess;
+  int cus = 0;
+  if (p.vt != nullptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipGetLastError();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    // A call whose blocks all run in the first round (one workgroup per CU)
+    // gains nothing from sharing them out by a counter, and V packing (one
+    // more launch and pass over V) costs it more than the transposing reads
+    // do: it reads V in place (bitwise the same results).
+    if (blocks <= cus) p.vt = nullptr;
+  }
   if (p.vt != nullptr) {
     // the work counter follows the packed tiles
     p.counter = vp.counter = reinterpret_cast<int*>(p.vt + vt_elems);
     const hipError_t e = launch_v_pack(vp, stream);
     if (e != hipSuccess) return e;
     // one persistent workgroup per CU (128 KB of LDS: one fits per CU)
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipGetLastError();
-    if (cus <= 0) return hipErrorInvalidDevice;
     hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)min(blocks, cus)), dim3(NT), 0, stream, p);
   } else {
     hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, p);

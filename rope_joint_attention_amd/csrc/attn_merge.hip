@@ -29,14 +29,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 template <int P>
-__device__ __forceinline__ void merge_chunk(const MergeParams& p, int64_t in_off, int64_t row_off,
-                                            int64_t lse_idx, int64_t elem, bool write_lse) {
+__device__ __forceinline__ void merge_chunk(const MergeParams& p, int64_t row_off, int64_t lse_idx,
+                                            int64_t elem, bool write_lse) {
   float l[P];
   u32x4 w[P];
 #pragma unroll
   for (int i = 0; i < P; ++i) {
     l[i] = p.lses[i][lse_idx];
-    w[i] = *reinterpret_cast<const u32x4*>(p.outs[i] + in_off + elem);
+    w[i] = *reinterpret_cast<const u32x4*>(p.outs[i] + row_off + elem);
   }
   float top = l[0];
 #pragma unroll
@@ -70,12 +70,11 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(MergeParams p) {
   const int b = (int)(row / p.seq_len);
   const int n = (int)(row - (int64_t)b * p.seq_len);
   const int64_t row_off = (int64_t)b * p.stride_b + (int64_t)n * p.stride_l;
-  const int64_t in_off = (int64_t)b * p.in_stride_b + (int64_t)n * p.in_stride_l;
   const int64_t lse_idx = ((int64_t)b * HV_HEADS + head) * p.seq_len + n;
   const int64_t elem = (int64_t)head * HV_HEAD_DIM + chunk * 8;
   const bool wl = p.lse_out != nullptr && chunk == 0;
   switch (p.n_parts) {
-#define HV_MERGE_CASE(P) case P: merge_chunk<P>(p, in_off, row_off, lse_idx, elem, wl); break;
+#define HV_MERGE_CASE(P) case P: merge_chunk<P>(p, row_off, lse_idx, elem, wl); break;
     HV_MERGE_CASE(1) HV_MERGE_CASE(2) HV_MERGE_CASE(3) HV_MERGE_CASE(4)
     HV_MERGE_CASE(5) HV_MERGE_CASE(6) HV_MERGE_CASE(7) HV_MERGE_CASE(8)
     HV_MERGE_CASE(9) HV_MERGE_CASE(10) HV_MERGE_CASE(11) HV_MERGE_CASE(12)

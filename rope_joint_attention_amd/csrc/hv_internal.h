@@ -147,18 +147,15 @@ struct VtParams {
 hipError_t launch_v_pack(const VtParams& p, hipStream_t stream);
 
 // ---- merge of partial attention results -------------------------------------
-// n_parts outputs over disjoint key blocks (rows at in_stride_b / in_stride_l;
-// out at stride_b / stride_l) and their
+// n_parts outputs over disjoint key blocks (same layout as out) and their
 // log-sum-exps ([batch][24][seq_len] fp32) combine into out / lse_out.
 struct MergeParams {
   const uint16_t* outs[HV_MAX_MERGE_PARTS];
   const float* lses[HV_MAX_MERGE_PARTS];
   uint16_t* out;
   float* lse_out;      // may be null
-  int64_t stride_b;    // elements, out
-  int64_t stride_l;    // elements, out
-  int64_t in_stride_b; // elements, each of outs
-  int64_t in_stride_l; // elements, each of outs
+  int64_t stride_b;    // elements
+  int64_t stride_l;    // elements
   int32_t batch;
   int32_t seq_len;
   int32_t n_parts;

@@ -175,89 +175,6 @@ void rope_frequencies(float theta, float* freq) {
       freq[pair++] = (float)pow((double)theta, -2.0 * j / widths[a]);
 }
 
-// ---- key-range split of small forward calls ---------------------------------
-// A padded call with few query blocks (24 heads x ceil(seq_len / 256) per
-// batch entry) leaves most of the 256 CUs idle while each workgroup walks
-// every key tile of its block.  With a workspace, such a call is split: the
-// key range of every batch entry is cut into n parts of whole 64-key tiles,
-// each (part, entry) pair runs as a segment of one launch that writes its
-// partial output (bf16) and natural-log log-sum-exp into the workspace, and
-// the merge kernel combines the parts exactly (notes page section 9.2 for the
-// combination: the same one Ring Attention uses for K/V blocks).
-constexpr int kSplitMaxBlocks = 128;   // calls with at most this many query blocks
-constexpr int kSplitTargetBlocks = 256;
-constexpr int kSplitMaxParts = 8;
-constexpr int64_t kSplitMaxRows = 5 * 256;  // 24 * B * ceil(L / 256) <= 128 implies B * L <= 1280
-constexpr int64_t kSplitRowBytes = (int64_t)HV_HEADS * HV_HEAD_DIM * 2 + HV_HEADS * 4;
-
-// Parts to split the padded call of p (batch entries as its segments) into,
-// or 1 when it is not split.
-int split_parts(const hv::AttnParams& p, int seq_len) {
-  const int64_t blocks = (int64_t)HV_HEADS * p.n_seg * ((seq_len + 255) / 256);
-  if (blocks == 0 || blocks > kSplitMaxBlocks) return 1;
-  int parts = (int)(kSplitTargetBlocks / blocks);
-  if (parts > kSplitMaxParts) parts = kSplitMaxParts;
-  int nt_max = 0;
-  for (int b = 0; b < p.n_seg; ++b) {
-    const int nt = (p.seg[b].k_len + 63) / 64;
-    if (nt < parts) parts = nt;  // every part of every entry gets a tile
-    if (nt > nt_max) nt_max = nt;
-  }
-  if (parts <= 1) return 1;
-  // the longest part sets the time: as few parts as give it that length
-  const int per = (nt_max + parts - 1) / parts;
-  return (nt_max + per - 1) / per;
-}
-
-// Run the padded call of p split into `parts` over the keys (see above):
-// the workspace holds parts x [B][L][24][128] bf16 partial outputs, then
-// parts x [B][24][L] fp32 log-sum-exps.
-hipError_t launch_split(const hv::AttnParams& base, int parts, int seq_len, int64_t stride_b,
-                        int64_t stride_l, void* workspace, hipStream_t stream) {
-  const int B = base.n_seg, L = seq_len;
-  const int64_t rows = (int64_t)B * L;
-  uint16_t* part_out = static_cast<uint16_t*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(part_out + parts * rows * HV_HEADS * HV_HEAD_DIM);
-  hv::AttnParams sp = base;
-  sp.n_seg = parts * B;
-  sp.out = part_out;
-  sp.o_sl = (int64_t)HV_HEADS * HV_HEAD_DIM;
-  sp.lse = part_lse;
-  sp.lse_hstride = L;
-  sp.vt = nullptr;  // V read in place: no packing pass for a call this small
-  for (int j = 0; j < parts; ++j)
-    for (int b = 0; b < B; ++b) {
-      const hv::AttnSegment& s0 = base.seg[b];
-      const int nt = (s0.k_len + 63) / 64;
-      const int k0 = 64 * (int)((int64_t)j * nt / parts);
-      const int k1 = min(64 * (int)((int64_t)(j + 1) * nt / parts), s0.k_len);
-      hv::AttnSegment& sg = sp.seg[j * B + b];
-      sg = s0;
-      sg.k_off = s0.k_off + (int64_t)k0 * base.kv_sl;
-      sg.k_len = k1 - k0;
-      sg.o_off = ((int64_t)j * B + b) * L * HV_HEADS * HV_HEAD_DIM;
-      sg.lse_off = ((int64_t)j * B + b) * HV_HEADS * L;
-    }
-  hipError_t e = hv::launch_attn_fwd(sp, stream);
-  if (e != hipSuccess) return e;
-  hv::MergeParams mp;
-  memset(&mp, 0, sizeof(mp));
-  for (int j = 0; j < parts; ++j) {
-    mp.outs[j] = part_out + j * rows * HV_HEADS * HV_HEAD_DIM;
-    mp.lses[j] = part_lse + j * rows * HV_HEADS;
-  }
-  mp.n_parts = parts;
-  mp.out = base.out;
-  mp.lse_out = nullptr;
-  mp.stride_b = stride_b;
-  mp.stride_l = stride_l;
-  mp.in_stride_b = (int64_t)L * HV_HEADS * HV_HEAD_DIM;
-  mp.in_stride_l = (int64_t)HV_HEADS * HV_HEAD_DIM;
-  mp.batch = B;
-  mp.seq_len = L;
-  return hv::launch_attn_merge(mp, stream);
-}
-
 // Segment table of the padded batch for the backward: entry b's queries
 // attend to its first n_video + text_valid_len[b] keys.
 int padded_bwd_segments(hv::BwdParams& p, const int32_t* text_valid_len, int64_t n_video,
@@ -318,11 +235,7 @@ int hv_version(void) { return 10200; }
 int64_t hv_attention_workspace_bytes(int64_t n_keys, int32_t n_segments) {
   if (n_keys < 0 || n_segments < 0) return 0;
   const int64_t tiles = (n_keys + 63 * (int64_t)n_segments) / 64;
-  const int64_t packed = tiles > 0 ? tiles * HV_HEADS * hv::kVtTileElems * 2 + hv::kCounterBytes : 0;
-  // a padded call small enough to be split over its keys (batch * seq_len <=
-  // kSplitMaxRows) holds up to kSplitMaxParts partial results instead
-  const int64_t split = n_keys <= kSplitMaxRows ? kSplitMaxParts * n_keys * kSplitRowBytes : 0;
-  return packed > split ? packed : split;
+  return tiles > 0 ? tiles * HV_HEADS * hv::kVtTileElems * 2 + hv::kCounterBytes : 0;
 }
 
 const char* hv_status_string(int status) {
@@ -480,15 +393,6 @@ int hv_joint_attention_fwd(const hv_bf16* q, const hv_bf16* k, const hv_bf16* v,
   p.vt = (uint16_t*)workspace;
   p.q_sl = p.kv_sl = p.o_sl = layout->stride_l;
   p.scale_log2 = scale_log2(softmax_scale);
-  if (workspace) {
-    const int parts = split_parts(p, layout->seq_len);
-    const int64_t need = parts * (int64_t)layout->batch * layout->seq_len * kSplitRowBytes;
-    if (parts > 1 && workspace_bytes >= need) {
-      const hipError_t e = launch_split(p, parts, layout->seq_len, layout->stride_b,
-                                        layout->stride_l, workspace, (hipStream_t)stream);
-      return e == hipSuccess ? HV_OK : HV_ERR_HIP;
-    }
-  }
   const hipError_t e = hv::launch_attn_fwd(p, (hipStream_t)stream);
   return e == hipSuccess ? HV_OK : HV_ERR_HIP;
 }
@@ -721,8 +625,8 @@ int hv_attention_merge(const hv_bf16* const* outs, const float* const* lses, int
   p.n_parts = n_parts;
   p.out = out;
   p.lse_out = lse_out;
-  p.stride_b = p.in_stride_b = layout->stride_b;
-  p.stride_l = p.in_stride_l = layout->stride_l;
+  p.stride_b = layout->stride_b;
+  p.stride_l = layout->stride_l;
   p.batch = layout->batch;
   p.seq_len = layout->seq_len;
   const hipError_t e = hv::launch_attn_merge(p, (hipStream_t)stream);

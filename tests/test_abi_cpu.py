@@ -481,14 +481,7 @@ COUNTER = 256                        # the attention's work counter after the pa
     (2 * 300, 2, 11), (100, 3, 4), (-1, 1, 0), (5, -1, 0),   # floor((n + 63 s) / 64) tiles
 ])
 def test_workspace_bytes(n_keys, n_seg, tiles):
-    packed = tiles * TILE_BYTES + COUNTER if tiles else 0
-    # a padded call of at most 1280 rows may be split over its keys into up to
-    # 8 partial results: 24 * 128 bf16 outputs and 24 fp32 log-sum-exps per row
-    split = 8 * n_keys * SPLIT_ROW_BYTES if 0 <= n_keys <= 1280 and n_seg >= 0 else 0
-    assert hv.hv_attention_workspace_bytes(n_keys, n_seg) == max(packed, split)
-
-
-SPLIT_ROW_BYTES = 24 * 128 * 2 + 24 * 4
+    assert hv.hv_attention_workspace_bytes(n_keys, n_seg) == (tiles * TILE_BYTES + COUNTER if tiles else 0)
 
 
 def test_workspace_bound_covers_every_split():

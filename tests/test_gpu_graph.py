@@ -2,8 +2,8 @@
 (torch.cuda.CUDAGraph) and replayed.
 
 The captured sequence is hv_joint_attention_fwd with a packed-V workspace,
-the same call on a small batch that it splits over the keys (attention into
-partial results, then the merge kernel), hv_attention_fwd_lse with the first
+the same call on a small batch (one round of query blocks, so it reads V in
+place with one workgroup per block), hv_attention_fwd_lse with the first
 workspace and hv_joint_attention_bwd with its delta workspace.  Both workspaces hold work counters that the persistent
 workgroups draw blocks from; the calls reset them with a kernel of their own
 (no memset node is recorded), so every replay must redo the whole work.  Each
@@ -24,7 +24,7 @@ def test_graph_replays_match_eager_calls():
     import torch
     import rope_joint_attention_amd as hv
 
-    B, L, N, valid = 2, 700, 600, [60, 13]
+    B, L, N, valid = 2, 1400, 1300, [60, 13]   # 288 query blocks: V is packed
     lk = [N + x for x in valid]
     shape = (B, L, hv.HV_HEADS, hv.HV_HEAD_DIM)
     q, k, v, g = (torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(4))
@@ -33,7 +33,7 @@ def test_graph_replays_match_eager_calls():
     ws = torch.empty(hv.hv_attention_workspace_bytes(B * L, B), dtype=torch.uint8, device="cuda")
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     delta = torch.empty(2 * B * hv.HV_HEADS * L + hv.BWD_COUNTER_FLOATS, dtype=torch.float32, device="cuda")
-    # a small call (48 query blocks, 8 key tiles): split over its keys
+    # a small call (48 query blocks, 8 key tiles): V read in place
     Ls, Ns, valid_s = 512, 256, [200]
     qs, ks, vs = (torch.empty((1, Ls, hv.HV_HEADS, hv.HV_HEAD_DIM), dtype=torch.bfloat16, device="cuda")
                   for _ in range(3))
@@ -82,6 +82,6 @@ def test_graph_replays_match_eager_calls():
         e_g = hv.hv_joint_attention_bwd(q, k, v, e_l, g, e_lse, valid, N)
         torch.cuda.synchronize()
         want = [torch_to_bits(t) for t in (e_j, e_s, e_l, *e_g)]
-        for name, a, b in zip(("out", "out (split call)", "out (lse form)", "dq", "dk", "dv"), got, want):
+        for name, a, b in zip(("out", "out (small call)", "out (lse form)", "dq", "dk", "dv"), got, want):
             assert np.array_equal(a, b), f"replay {seed}: {name} differs from the eager call"
         assert np.array_equal(got_lse, e_lse.cpu().numpy().view(np.uint32)), f"replay {seed}: lse"

@@ -5,8 +5,9 @@ hv_joint_attention_varlen_fwd first rewrite V tile by tile channel-major into
 it and read each P V operand with one 16-byte LDS read; without one they read
 V in place with the transposing LDS read.  Both feed the same values into the
 same MFMA slots, so the outputs (and log-sum-exps) must agree bit for bit.
-(Small padded calls given room for it take the key-range split instead; the
-tests here size the workspace for packing alone where they compare paths.)
+Calls whose query blocks all fit in one round of workgroups (at most one per
+CU: 256 on MI355X) read V in place even with a workspace, so the shapes here
+carry enough batch entries or rows to make the call pack.
 
 * bitwise agreement of the two paths on small shapes around the 64-key tile
   (ragged tails, one key, exact multiples of 64, batch entries with different
@@ -57,24 +58,28 @@ def expected_packed(vbits, k_lens, k_offs):
 
 
 SHAPES = [
-    # batch, n_video, text capacity, valid text per batch entry
-    (1, 1, 0, [0]),            # one key
-    (1, 40, 24, [24]),         # exactly one tile
-    (1, 40, 25, [24]),         # 64 keys, one padded row
-    (2, 63, 2, [0, 2]),        # keys 63 and 65
-    (1, 200, 57, [13]),
-    (3, 300, 45, [45, 3, 0]),
-    (1, 2047, 256, [255]),
+    # batch, n_video, text capacity, valid text per batch entry; every shape
+    # has more than 256 query blocks of 256 rows (24 per entry and 256 rows)
+    (11, 1, 0, [0] * 11),                        # one key
+    (11, 40, 24, [24] * 11),                     # exactly one tile
+    (11, 40, 25, [24, 25] * 5 + [0]),            # 64 keys, one padded row
+    (11, 63, 2, [0, 2] * 5 + [1]),               # keys 63 and 65
+    (6, 200, 57, [13, 57, 0, 1, 56, 30]),
+    (6, 300, 45, [45, 3, 0, 44, 1, 2]),
+    (2, 2047, 256, [255, 1]),
 ]
 
 
 def packed_workspace(n_video, valid):
-    """A workspace of exactly the packed-V size: enough for the packed path,
-    too small for the key-range split of small calls, so the call packs V."""
+    """A workspace of exactly the packed-V size."""
     import torch
 
     need = sum((n_video + x + 63) // 64 for x in valid) * 24 * TILE * 2 + 256
     return torch.empty(need, dtype=torch.uint8, device="cuda")
+
+
+def blocks_of(B, L):
+    return 24 * B * ((L + 255) // 256)
 
 
 @pytest.mark.parametrize("B,n_video,cap,valid", SHAPES, ids=lambda x: str(x))
@@ -83,6 +88,7 @@ def test_packed_and_inplace_paths_agree_bitwise(B, n_video, cap, valid):
     import rope_joint_attention_amd as hv
 
     L = n_video + cap
+    assert blocks_of(B, L) > 256
     bits = hvinputs.draw_qkv(B, L, seed=31 * L + B)
     q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
     log(f"packed vs in-place B={B} N={n_video} L={L} valid={valid}")
@@ -98,11 +104,11 @@ def test_lse_form_agrees_bitwise():
     import torch
     import rope_joint_attention_amd as hv
 
-    bq = hvinputs.draw_qkv(2, 300, seed=91)
+    bq = hvinputs.draw_qkv(2, 1400, seed=91)      # 2 x 6 x 24 = 288 query blocks
     bk = hvinputs.draw_qkv(2, 517, seed=92)
     q = bits_to_torch(bq["q"])
     k, v = bits_to_torch(bk["k"]), bits_to_torch(bk["v"])
-    log("packed vs in-place: lse form, 300 queries x 517 keys, valid 517 / 130")
+    log("packed vs in-place: lse form, 1400 queries x 517 keys, valid 517 / 130")
     oa, la = hv.hv_attention_fwd_lse(q, k, v, [517, 130], pack_v=True)
     ob, lb = hv.hv_attention_fwd_lse(q, k, v, [517, 130], pack_v=False)
     torch.cuda.synchronize()
@@ -114,27 +120,29 @@ def test_varlen_form_agrees_bitwise():
     import torch
     import rope_joint_attention_amd as hv
 
-    T = 700
+    T = 3700
     bits = hvinputs.draw_qkv(1, T, seed=93)
     q, k, v = (bits_to_torch(bits[n][0]) for n in ("q", "k", "v"))
-    cq = [0, 130, 130, 400, 650]
-    ck = [0, 200, 260, 300, 700]   # segment 1 has keys but no queries
+    cq = [0, 1300, 1300, 2700, 3650]   # 6 + 6 + 4 query blocks per head: 384
+    ck = [0, 2000, 2600, 3000, 3700]   # segment 1 has keys but no queries
     log(f"packed vs in-place: varlen cu_q={cq} cu_k={ck}")
     oa, la = hv.hv_joint_attention_varlen_fwd(q, k, v, cq, ck, want_lse=True, pack_v=True)
     ob, lb = hv.hv_joint_attention_varlen_fwd(q, k, v, cq, ck, want_lse=True, pack_v=False)
     torch.cuda.synchronize()
     a, b = torch_to_bits(oa), torch_to_bits(ob)
-    assert np.array_equal(a[:650], b[:650])
+    assert np.array_equal(a[:3650], b[:3650])
     la, lb = la.cpu().numpy(), lb.cpu().numpy()
-    assert np.array_equal(la[:, :650].view(np.uint32), lb[:, :650].view(np.uint32))
+    assert np.array_equal(la[:, :3650].view(np.uint32), lb[:, :3650].view(np.uint32))
 
 
 def test_workspace_holds_the_packed_layout():
     import torch
     import rope_joint_attention_amd as hv
 
-    B, n_video, cap, valid = 2, 150, 40, [40, 7]     # 190 and 157 keys: 3 tiles each
+    B, n_video, cap = 12, 150, 40                    # 12 x 24 = 288 query blocks
+    valid = [40, 7] * 6                              # 190 and 157 keys: 3 tiles each
     L = n_video + cap
+    assert blocks_of(B, L) > 256
     bits = hvinputs.draw_qkv(B, L, seed=94)
     vb = bits["v"].copy()
     vb[1, n_video + 7:] = 0x7FC0                     # NaN in the padded rows of entry 1
@@ -142,9 +150,6 @@ def test_workspace_holds_the_packed_layout():
     need = sum((n_video + x + 63) // 64 for x in valid) * 24 * TILE * 2 + 256
     cap_bytes = hv.hv_attention_workspace_bytes(B * L, B)
     assert cap_bytes >= need
-    # 1 KB more than the packed layout needs: too little for the key-range
-    # split this small call would otherwise take, so V is packed
-    cap_bytes = need + 1024
     ws = torch.full((cap_bytes // 2,), 0x1234, dtype=torch.int16, device="cuda")
     log(f"packed layout B={B} L={L} valid={valid}: need {need} bytes of {cap_bytes}")
     out = hv.hv_joint_attention_fwd(q, k, v, valid, n_video, workspace=ws)
@@ -168,10 +173,10 @@ def test_varlen_workspace_layout_skips_segments_without_queries():
     import torch
     import rope_joint_attention_amd as hv
 
-    T = 400
+    T = 3100
     bits = hvinputs.draw_qkv(1, T, seed=95)
     q, k, v = (bits_to_torch(bits[n][0]) for n in ("q", "k", "v"))
-    cq = [0, 100, 100, 300]
+    cq = [0, 1500, 1500, 3000]      # 6 + 6 query blocks per head: 288
     ck = [0, 70, 200, 330]          # segment 1: 130 keys, no queries -> not packed
     ws = torch.zeros(hv.hv_attention_workspace_bytes(T, 3) // 2, dtype=torch.int16, device="cuda")
     log("varlen packed layout with a query-less segment")
@@ -185,15 +190,15 @@ def test_varlen_workspace_layout_skips_segments_without_queries():
 def test_workspace_reused_by_consecutive_calls():
     # the second (smaller) call finds the first one's packed tiles and counter
     # in the workspace and must not depend on them: it matches the same call
-    # on a fresh NaN-filled workspace bit for bit.  The first call packs V;
-    # the second is small enough to be split over its keys.
+    # on a fresh NaN-filled workspace bit for bit.  Both calls pack V.
     import torch
     import rope_joint_attention_amd as hv
 
-    nbytes = max(hv.hv_attention_workspace_bytes(1300, 1), hv.hv_attention_workspace_bytes(333, 1))
+    nbytes = hv.hv_attention_workspace_bytes(2 * 1300, 2)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    for L, valid, seed in ((1300, [100], 96), (333, [17], 97)):
-        bits = hvinputs.draw_qkv(1, L, seed=seed)
+    for B, L, valid, seed in ((2, 1300, [100, 7], 96), (3, 900, [17, 0, 120], 97)):
+        assert blocks_of(B, L) > 256
+        bits = hvinputs.draw_qkv(B, L, seed=seed)
         q, k, v = (bits_to_torch(bits[n]) for n in ("q", "k", "v"))
         n_video = L - 120
         log(f"workspace reuse L={L}")

@@ -165,14 +165,12 @@ def test_varlen_packed_clips():
     ref, lref = varlen_attention(widen(bits["q"][0]), widen(bits["k"][0]), widen(bits["v"][0]), cu, cu)
     assert_close(widen(torch_to_bits(out)), ref, "varlen clips out")
     lse_close(lse.cpu().numpy(), lref, "varlen clips")
-    # each clip equals the joint attention call on that clip alone (without a
-    # workspace: a call this small would otherwise be split over its keys,
-    # which rounds its partial results, while a packed segment is not split)
+    # each clip equals the joint attention call on that clip alone
     for s, ((F, H, W, t), g) in enumerate(zip(clips, grids)):
         a, b = cu[s], cu[s + 1]
         sl = slice(a, b)
         one = hv.hv_joint_attention_fwd(q[None, sl].contiguous(), k[None, sl].contiguous(),
-                                        v[None, sl].contiguous(), [t], g.n_video, pack_v=False)
+                                        v[None, sl].contiguous(), [t], g.n_video)
         torch.cuda.synchronize()
         assert torch.equal(one[0], out[sl]), f"clip {s} differs from its own joint call"
 
