@@ -228,9 +228,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const int hh = lane >> 5;
 
   const int nb = p.n_blocks;
-  __shared__ int s_block;
+  // block ids of the persistent workgroups: slot iter % 2 holds this
+  // iteration's, slot (iter + 1) % 2 receives the next one
+  __shared__ int s_block[2];
   for (int iter = 0;; ++iter) {
   int logical;
+  int next_block = 0;  // thread 0: the id taken for the next iteration
   if constexpr (kPackedV) {
     // Persistent workgroups, one per CU, take query blocks in order from a
     // counter in the workspace (zeroed by the packing kernel).  Under MFMA
@@ -238,12 +241,18 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     // on one part); with a fixed share of blocks per XCD the slowest one sets
     // the time, with the counter the faster ones take more blocks.  Blocks are
     // numbered segment by segment, head by head, so the 256 blocks in flight
-    // share one head's K/V.
-    __syncthreads();  // the previous block is done with LDS and s_block
-    if (tid == 0) s_block = atomicAdd(p.counter, 1);
-    __syncthreads();
-    logical = __builtin_amdgcn_readfirstlane(s_block);
+    // share one head's K/V.  The next block is taken as soon as this one
+    // starts (its round trip overlaps the block's first loads) and published
+    // in LDS at the end of the block, before the barrier of the end-of-block
+    // check, which orders it before the next iteration's read; the next
+    // iteration publishes into the other slot.
+    if (iter == 0) {
+      if (tid == 0) s_block[0] = atomicAdd(p.counter, 1);
+      __syncthreads();
+    }
+    logical = __builtin_amdgcn_readfirstlane(s_block[iter & 1]);
     if (logical >= nb) break;
+    if (tid == 0) next_block = atomicAdd(p.counter, 1);
   } else {
     // One block per workgroup.  Workgroups are dealt round-robin to the 8
     // XCDs; give each XCD a contiguous range of (segment, head, query-block)
@@ -636,11 +645,17 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   };  // run
 
   run(std::false_type{});
+  if constexpr (kPackedV) {
+    if (tid == 0) s_block[(iter + 1) & 1] = next_block;
+  }
   float l_tot = sum_across_halves(l_run);
   // every wave of the block joins (the waves share the K/V tiles in LDS)
   if (__syncthreads_or(!(l_tot < 0x1p64f))) {
     run(std::true_type{});
     l_tot = sum_across_halves(l_run);
+    // the next block's first tile loads must not overwrite LDS that a slower
+    // wave of this block still reads
+    __syncthreads();
   }
 
   // ---- epilogue: O / l, round to bf16, store rows that exist; optionally
