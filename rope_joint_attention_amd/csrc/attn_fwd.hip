@@ -16,7 +16,9 @@
 //
 // Work decomposition
 //   * one query block = (segment, head, 256 query rows); 8 waves of 32 rows,
-//     two waves per SIMD, one workgroup per CU.  With a workspace the
+//     two waves per SIMD, one workgroup per CU (calls small enough that
+//     blocks of 128 rows all run at once use those instead, 4 waves, one per
+//     SIMD: see kWavesSmall).  With a workspace the
 //     workgroups are persistent (one per CU) and take query blocks from a
 //     counter; without one each workgroup does one block;
 //   * K and V tiles of 64 keys reach LDS by direct global->LDS loads
@@ -78,10 +80,25 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = HV_HEAD_DIM;  // 128
 constexpr int BN = 64;          // keys per tile
-constexpr int NW = 8;           // waves per workgroup
 constexpr int QPW = 32;         // query rows per wave
-constexpr int BM = NW * QPW;    // 256 query rows per workgroup
-constexpr int NT = NW * 64;     // 512 threads
+// Waves per workgroup: 8 (256 query rows, two waves per SIMD) for every call
+// whose blocks take more than one round of workgroups; 4 (128 rows, one wave
+// per SIMD) when even the 128-row blocks all run in the first round, where a
+// block's time is the chain of its key tiles and one wave per SIMD runs each
+// tile in half the time.
+constexpr int kWavesLarge = 8;
+constexpr int kWavesSmall = 4;
+// Per wave count W: 1-KB load instructions per wave and tile, and the tile
+// rows each wave loads.  (Namespace-scope templates rather than constants
+// local to the kernel: the host pass of this compiler fails to instantiate a
+// kernel template whose lambdas use such local constants, and then silently
+// emits no launch stub for it.)
+template <int W> constexpr int kLoadsPerWave = 16 / W;
+template <int W> constexpr int kRowsPerWave = 64 / W;
+// Per-lane load offsets are held in arrays of the largest count (the 8-wave
+// kernel leaves the upper half unused): with a bound that depends on the
+// kernel's wave count, the host pass drops the kernel as well.
+constexpr int kMaxLoadsPerWave = 16 / kWavesSmall;
 constexpr int NSTAGE = 4;       // K/V tiles resident in LDS (each)
 constexpr int ROWB = D * 2;     // bytes per K/V row in LDS (no padding; swizzled)
 constexpr int TILEB = BN * ROWB;                 // 16 KB per K or V tile
@@ -196,8 +213,8 @@ __device__ __forceinline__ void bound_weights(float& m_run, float& l_run, f32x16
   }
 }
 
-template <bool kPackedV>
-__global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
+template <bool kPackedV, int kNW>
+__global__ __launch_bounds__(kNW * 64, 1) void attn_fwd_kernel(AttnParams p) {
   // One LDS array per stage: with every access naming its array at compile
   // time, the compiler can tell the tile being loaded from the tiles being
   // read and does not drain the in-flight global->LDS loads before the
@@ -282,7 +299,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   const uint16_t* Vt = kPackedV ? p.vt + sg.vt_off + (int64_t)head * ntiles * kVtTileElems : nullptr;
 
   // Q^T operand: lane holds query row q0 + l32, channels 16*kc + 8*hh .. +7.
-  const int q0 = qb * BM + wave * QPW;
+  const int q0 = qb * (kNW * QPW) + wave * QPW;
   const int qrow = min(q0 + l32, L - 1);  // rows past the end are computed, never stored
   bf16x8 qf[8];
   {
@@ -298,46 +315,59 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // still read its 256 contiguous bytes.  Byte offsets from the tile's first
   // row are fixed per lane (32 bits: a tile spans 64 rows), so a full tile
   // costs no vector arithmetic; only the last, partial tile clamps its rows.
-  const int ld_row0 = 8 * wave + (lane >> 4);
-  const int ld_kc0 = (lane & 15) ^ (ld_row0 & 15);
-  const int ld_kc1 = (lane & 15) ^ ((ld_row0 + 4) & 15);
-  const int ld_vc = (lane & 15) ^ ((ld_row0 & 3) << 2);  // rows 4 apart swizzle alike
+  // Wave w issues instructions kLoadsPerWave<kNW>*w .. kLoadsPerWave<kNW>*w + kLoadsPerWave<kNW>-1 of a tile: rows
+  // kRowsPerWave<kNW>*w + 4j + l/16 for its instruction j.
+  const int ld_row0 = kRowsPerWave<kNW> * wave + (lane >> 4);
   const uint32_t row_bytes = (uint32_t)(sl * 2);
-  const uint32_t lk0 = ld_row0 * row_bytes + ld_kc0 * 16, lk1 = (ld_row0 + 4) * row_bytes + ld_kc1 * 16;
-  const uint32_t lv0 = ld_row0 * row_bytes + ld_vc * 16, lv1 = (ld_row0 + 4) * row_bytes + ld_vc * 16;
-  auto load_tile = [&](const uint16_t* g, unsigned char* buf, int tile, uint32_t o0, uint32_t o1,
-                       int c0, int c1) {
+  int ld_kc[kMaxLoadsPerWave], ld_vc[kMaxLoadsPerWave];
+  uint32_t lk[kMaxLoadsPerWave], lv[kMaxLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave<kNW>; ++j) {
+    ld_kc[j] = (lane & 15) ^ ((ld_row0 + 4 * j) & 15);
+    ld_vc[j] = (lane & 15) ^ ((ld_row0 & 3) << 2);  // rows 4 apart swizzle alike
+    lk[j] = (ld_row0 + 4 * j) * row_bytes + ld_kc[j] * 16;
+    lv[j] = (ld_row0 + 4 * j) * row_bytes + ld_vc[j] * 16;
+  }
+  auto load_tile = [&](const uint16_t* g, unsigned char* buf, int tile, const uint32_t (&o)[kMaxLoadsPerWave],
+                       const int (&c)[kMaxLoadsPerWave]) {
     const unsigned char* tb = (const unsigned char*)(g + (int64_t)tile * BN * sl);
-    unsigned char* dst = buf + wave * 2048;
+    unsigned char* dst = buf + wave * (kLoadsPerWave<kNW> * 1024);
     if (tile * BN + BN > Lk) {  // partial last tile: clamp to the last valid row
       const int lim = Lk - 1 - tile * BN;
-      const uint32_t c0o = (uint32_t)min(ld_row0, lim) * row_bytes + c0 * 16;
-      const uint32_t c1o = (uint32_t)min(ld_row0 + 4, lim) * row_bytes + c1 * 16;
-      __builtin_amdgcn_global_load_lds(tb + c0o, (HV_LDS void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(tb + c1o, (HV_LDS void*)(dst + 1024), 16, 0, 0);
+      uint32_t co[kMaxLoadsPerWave];
+#pragma unroll
+      for (int j = 0; j < kLoadsPerWave<kNW>; ++j) co[j] = (uint32_t)min(ld_row0 + 4 * j, lim) * row_bytes + c[j] * 16;
+#pragma unroll
+      for (int j = 0; j < kLoadsPerWave<kNW>; ++j)
+        __builtin_amdgcn_global_load_lds(tb + co[j], (HV_LDS void*)(dst + j * 1024), 16, 0, 0);
     } else {
-      __builtin_amdgcn_global_load_lds(tb + o0, (HV_LDS void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(tb + o1, (HV_LDS void*)(dst + 1024), 16, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kLoadsPerWave<kNW>; ++j)
+        __builtin_amdgcn_global_load_lds(tb + o[j], (HV_LDS void*)(dst + j * 1024), 16, 0, 0);
     }
   };
-  auto load_k = [&](auto st, int tile) { load_tile(Kg, kbuf(st), tile, lk0, lk1, ld_kc0, ld_kc1); };
-  // Packed V tile: 128 rows of 128 bytes, instruction i = 2w + j covers rows
-  // 8i .. 8i+7; lane l fills slot l%8 of row 8i + l/8 with the chunk the
+  auto load_k = [&](auto st, int tile) { load_tile(Kg, kbuf(st), tile, lk, ld_kc); };
+  // Packed V tile: 128 rows of 128 bytes, instruction i = kLoadsPerWave<kNW>*w + j covers
+  // rows 8i .. 8i+7; lane l fills slot l%8 of row 8i + l/8 with the chunk the
   // row's swizzle (slot c ^ ((row / 2) % 8)) puts there.  Full tiles only:
   // keys past the end are zeros in the workspace.
-  uint32_t lt0 = (16 * wave + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 4)) << 4);
-  uint32_t lt1 = (16 * wave + 8 + (lane >> 3)) * 128 + (((lane & 7) ^ (4 + (lane >> 4))) << 4);
+  uint32_t lt[kMaxLoadsPerWave];
+#pragma unroll
+  for (int j = 0; j < kLoadsPerWave<kNW>; ++j)
+    lt[j] = (8 * (kLoadsPerWave<kNW> * wave + j) + (lane >> 3)) * 128 + (((lane & 7) ^ ((4 * j + (lane >> 4)) & 7)) << 4);
   auto load_v = [&](auto st, int tile) {
     if constexpr (kPackedV) {
       // opaque per call: keeps the scalar tile base + 32-bit lane offset form
       // instead of 64-bit per-lane addresses hoisted out of the loop
-      asm volatile("" : "+v"(lt0), "+v"(lt1));
+#pragma unroll
+      for (int j = 0; j < kLoadsPerWave<kNW>; ++j) asm volatile("" : "+v"(lt[j]));
       const unsigned char* tb = (const unsigned char*)(Vt + (int64_t)tile * kVtTileElems);
-      unsigned char* dst = vbuf(st) + wave * 2048;
-      __builtin_amdgcn_global_load_lds(tb + lt0, (HV_LDS void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(tb + lt1, (HV_LDS void*)(dst + 1024), 16, 0, 0);
+      unsigned char* dst = vbuf(st) + wave * (kLoadsPerWave<kNW> * 1024);
+#pragma unroll
+      for (int j = 0; j < kLoadsPerWave<kNW>; ++j)
+        __builtin_amdgcn_global_load_lds(tb + lt[j], (HV_LDS void*)(dst + j * 1024), 16, 0, 0);
     } else {
-      load_tile(Vg, vbuf(st), tile, lv0, lv1, ld_vc, ld_vc);
+      load_tile(Vg, vbuf(st), tile, lv, ld_vc);
     }
   };
 
@@ -463,10 +493,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   load_v(I1{}, min(1, ntiles - 1));
   load_v(I2{}, min(2, ntiles - 1));
   // Each wave's loads complete in the order issued: its eight Q loads, then
-  // two instructions per tile, K 0..3 and V 0..2.  Tile 0's scores wait only
-  // for Q and K tile 0 (12 instructions may still be in flight), so the first
+  // kLoadsPerWave<kNW> instructions per tile, K 0..3 and V 0..2.  Tile 0's scores wait only
+  // for Q and K tile 0 (six tiles may still be in flight), so the first
   // MFMAs start one tile's latency after the block begins instead of seven.
-  barrier_after<12>();
+  barrier_after<6 * kLoadsPerWave<kNW>>();
   f32x16 sa[2], sb[2];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
@@ -475,7 +505,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   }
   if (ntiles == 1) mask_tile(sa[0], sa[1], Lk, hh);
   update_reference(tile_max(sa[0], sa[1], c2), m_run, l_run, o);
-  barrier_after<10>();  // K tile 1 in place
+  barrier_after<5 * kLoadsPerWave<kNW>>();  // K tile 1 in place
   // K operands of the first step (tile 1) are read, and its first two QK^T
   // MFMAs issued, before its barrier (see the end of a step)
   bf16x8 kf[4];
@@ -490,7 +520,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
   // K tiles 2, 3 and V tile 0 in place for the first step (V tiles 1 and 2 may
   // still be in flight: the first step's barrier waits for them), and every
   // wave has read K tile 0 before its buffer is refilled
-  barrier_after<4>();
+  barrier_after<2 * kLoadsPerWave<kNW>>();
 
   // ---- steady state.  Step t (tile t+1 exists; U = t % 4 at compile time),
   // in fixed instruction order (sched_barrier fences between bundles keep the
@@ -593,9 +623,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(AttnParams p) {
     kf[0] = k_frag(KN{}, 0, 2);
     kf[1] = k_frag(KN{}, 1, 2);
     __builtin_amdgcn_sched_barrier(0);
-    // the 4 loads just issued stay in flight, and so may the two reads of K
+    // the loads just issued (two tiles) stay in flight, and so may the two reads of K
     // tile t+2 (its stage is not refilled before the next barrier)
-    barrier_after<4, 2>();
+    barrier_after<2 * kLoadsPerWave<kNW>, 2>();
     if constexpr (kTrack) update_reference(mx, m_run, l_run, o);
     else bound_weights(m_run, l_run, o);
   };
@@ -694,9 +724,32 @@ hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream) {
   vp.kv_sl = p.kv_sl;
   vp.n_seg = p.n_seg;
   vp.n_blocks = 0;
+  // query blocks of 128 rows (kWavesSmall) and of 256 rows (kWavesLarge)
+  int64_t blocks_small = 0, blocks_large = 0;
+  for (int i = 0; i < p.n_seg; ++i) {
+    blocks_small += HV_HEADS * ((p.seg[i].q_len + kWavesSmall * QPW - 1) / (kWavesSmall * QPW));
+    blocks_large += HV_HEADS * ((p.seg[i].q_len + kWavesLarge * QPW - 1) / (kWavesLarge * QPW));
+  }
+  int cus = 0;
+  if (blocks_large > 0) {
+    // compute units of the current device, looked up once per device
+    static int cu_count[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    cus = dev >= 0 && dev < 64 ? __atomic_load_n(&cu_count[dev], __ATOMIC_RELAXED) : 0;
+    if (cus <= 0) {
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipGetLastError();
+      if (cus <= 0) return hipErrorInvalidDevice;
+      if (dev >= 0 && dev < 64) __atomic_store_n(&cu_count[dev], cus, __ATOMIC_RELAXED);
+    }
+  }
+  // blocks of 128 query rows when they all fit in one round of workgroups
+  const bool small = blocks_small <= cus;
+  const int bm = (small ? kWavesSmall : kWavesLarge) * QPW;
   for (int i = 0; i < p.n_seg; ++i) {
     AttnSegment& sg = p.seg[i];
-    sg.nqb = (sg.q_len + BM - 1) / BM;
+    sg.nqb = (sg.q_len + bm - 1) / bm;
     sg.blk_begin = blocks;
     blocks += HV_HEADS * sg.nqb;
     // packed V only for segments with query rows
@@ -714,28 +767,22 @@ hipError_t launch_attn_fwd(AttnParams& p, hipStream_t stream) {
   }
   p.n_blocks = blocks;
   if (blocks == 0) return hipSuccess;
-  int cus = 0;
-  if (p.vt != nullptr) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipGetLastError();
-    if (cus <= 0) return hipErrorInvalidDevice;
-    // A call whose blocks all run in the first round (one workgroup per CU)
-    // gains nothing from sharing them out by a counter, and V packing (one
-    // more launch and pass over V) costs it more than the transposing reads
-    // do: it reads V in place (bitwise the same results).
-    if (blocks <= cus) p.vt = nullptr;
-  }
+  // A call whose blocks all run in the first round (one workgroup per CU)
+  // gains nothing from sharing them out by a counter, and V packing (one more
+  // launch and pass over V) costs it more than the transposing reads do: it
+  // reads V in place (bitwise the same results).
+  if (blocks <= cus) p.vt = nullptr;
   if (p.vt != nullptr) {
     // the work counter follows the packed tiles
     p.counter = vp.counter = reinterpret_cast<int*>(p.vt + vt_elems);
     const hipError_t e = launch_v_pack(vp, stream);
     if (e != hipSuccess) return e;
     // one persistent workgroup per CU (128 KB of LDS: one fits per CU)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3((unsigned)min(blocks, cus)), dim3(NT), 0, stream, p);
+    attn_fwd_kernel<true, kWavesLarge><<<dim3((unsigned)min(blocks, cus)), dim3(kWavesLarge * 64), 0, stream>>>(p);
+  } else if (small) {
+    attn_fwd_kernel<false, kWavesSmall><<<dim3((unsigned)blocks), dim3(kWavesSmall * 64), 0, stream>>>(p);
   } else {
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+    attn_fwd_kernel<false, kWavesLarge><<<dim3((unsigned)blocks), dim3(kWavesLarge * 64), 0, stream>>>(p);
   }
   return hipGetLastError();
 }

@@ -13,6 +13,8 @@ carry enough batch entries or rows to make the call pack.
   (ragged tails, one key, exact multiples of 64, batch entries with different
   valid lengths), on the log-sum-exp form with its own K/V length, and on
   packed segments with empty ones in between;
+* bitwise agreement of the 4-wave variant that calls with few query blocks
+  run (128-row blocks) with the 8-wave blocks of larger calls;
 * the workspace holds exactly the documented packed layout (per segment,
   head and tile: 128 channel rows of 64 keys, keys swapped in bits 2 and 3
   inside each group of 16, zeros past the valid keys), then the work counter
@@ -133,6 +135,35 @@ def test_varlen_form_agrees_bitwise():
     assert np.array_equal(a[:3650], b[:3650])
     la, lb = la.cpu().numpy(), lb.cpu().numpy()
     assert np.array_equal(la[:, :3650].view(np.uint32), lb[:, :3650].view(np.uint32))
+
+
+@pytest.mark.parametrize("na", [1, 333, 1100])
+def test_small_call_variant_agrees_bitwise(na):
+    # Calls whose 128-row query blocks all fit in one round of workgroups run a
+    # 4-wave variant of the kernel (one wave per SIMD).  A segment of na rows
+    # computed that way (a call on it alone: ceil(na / 128) * 24 <= 256
+    # blocks) equals the same segment computed inside a call that also holds a
+    # 4000-row segment (8 waves per block, packed and in place), bit for bit.
+    import torch
+    import rope_joint_attention_amd as hv
+
+    T = na + 4000
+    bits = hvinputs.draw_qkv(1, T, seed=900 + na)
+    q, k, v = (bits_to_torch(bits[n][0]) for n in ("q", "k", "v"))
+    cu = [0, na, T]
+    log(f"4-wave vs 8-wave blocks: segment of {na} rows, alone and beside 4000 rows")
+    big_p, lse_p = hv.hv_joint_attention_varlen_fwd(q, k, v, cu, want_lse=True, pack_v=True)
+    big_i, lse_i = hv.hv_joint_attention_varlen_fwd(q, k, v, cu, want_lse=True, pack_v=False)
+    one, lse_1 = hv.hv_joint_attention_varlen_fwd(q[:na].contiguous(), k[:na].contiguous(),
+                                                  v[:na].contiguous(), [0, na], want_lse=True)
+    torch.cuda.synchronize()
+    a = torch_to_bits(one)
+    for big, lse in ((big_p, lse_p), (big_i, lse_i)):
+        assert np.array_equal(torch_to_bits(big)[:na], a)
+        assert np.array_equal(lse[:, :na].cpu().numpy().view(np.uint32), lse_1.cpu().numpy().view(np.uint32))
+    ref = joint_attention(widen(bits["q"][:, :na]), widen(bits["k"][:, :na]), widen(bits["v"][:, :na]),
+                          na, [0])
+    assert_close(widen(a)[None], ref, f"4-wave blocks, {na} rows")
 
 
 def test_workspace_holds_the_packed_layout():

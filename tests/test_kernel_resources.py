@@ -25,8 +25,9 @@ pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.ex
 
 # kernel (demangled-name fragment) -> (waves per SIMD, most SGPRs spilled)
 BUDGET = {
-    "attn_fwd_kernelILb1": (2, 72),
-    "attn_fwd_kernelILb0": (2, 64),
+    "attn_fwd_kernelILb1ELi8": (2, 72),
+    "attn_fwd_kernelILb0ELi4": (1, 80),   # before the 8-wave entry: matched by fragment
+    "attn_fwd_kernelILb0ELi8": (2, 64),
     "attn_bwd_delta_kernel": (None, 0),
     "attn_bwd_dkdv_kernel": (1, 8),
     "attn_bwd_dq_kernel": (2, 8),
