@@ -161,7 +161,10 @@ int hv_qk_norm_rope3d_apply(hv_bf16* q, hv_bf16* k, const hv_layout* layout,
  * blocks (24 heads x ceil(rows / 256) per segment) all fit in one round of
  * workgroups (at most one per compute unit) reads V in place even with a
  * workspace: there is nothing to share out, and packing would cost one more
- * launch and pass over V; the results are the same bit for bit.
+ * launch and pass over V; the results are the same bit for bit.  When even
+ * blocks of 128 query rows all fit in one round, those are used (four waves
+ * per workgroup instead of eight, each key tile then takes about half the
+ * time), again with bitwise the same results.
  * hv_attention_workspace_bytes(n_keys, n_segments) returns an upper bound
  * for n_keys keys in all over n_segments segments:
  *   hv_joint_attention_fwd         n_keys = batch * seq_len, n_segments = batch
