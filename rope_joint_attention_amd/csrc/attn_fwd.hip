@@ -309,14 +309,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void attn_fwd_kernel(AttnParams p) {
   }
 
   // ---- global -> LDS tile loads.  A tile is 16 wave instructions of 4 rows
-  // (1 KB); wave w issues instructions 2w and 2w+1 of each K and V tile.
+  // (1 KB); with n = 16 / kNW instructions per wave (2 for 8 waves, 4 for 4),
+  // wave w issues instructions n*w .. n*w + n-1 of each K and V tile, whose
+  // rows are (64 / kNW)*w + 4j + l/16 for its instruction j.
   // Lane l of an instruction fills LDS slot l%16 of row 4i + l/16, i.e. it
   // loads the chunk the row's swizzle puts in that slot; the 16 lanes of a row
   // still read its 256 contiguous bytes.  Byte offsets from the tile's first
   // row are fixed per lane (32 bits: a tile spans 64 rows), so a full tile
   // costs no vector arithmetic; only the last, partial tile clamps its rows.
-  // Wave w issues instructions kLoadsPerWave<kNW>*w .. kLoadsPerWave<kNW>*w + kLoadsPerWave<kNW>-1 of a tile: rows
-  // kRowsPerWave<kNW>*w + 4j + l/16 for its instruction j.
   const int ld_row0 = kRowsPerWave<kNW> * wave + (lane >> 4);
   const uint32_t row_bytes = (uint32_t)(sl * 2);
   int ld_kc[kMaxLoadsPerWave], ld_vc[kMaxLoadsPerWave];
