@@ -66,6 +66,13 @@ def test_token_grid_printed_values():
             assert (g.gt, g.gh, g.gw) == tuple(c["token_grid"])
 
 
+@pytest.mark.parametrize("fhw,n", [((129, 1104, 832), 118404), ((129, 624, 832), 66924),
+                                   ((129, 720, 720), 66825), ((129, 960, 960), 118800)])
+def test_token_grid_hand_worked_counts(fhw, n):
+    # 33 x (H/16) x (W/16), worked by hand: 33*69*52, 33*39*52, 33*45*45, 33*60*60
+    assert hv.hv_token_grid(*fhw).n_video == n
+
+
 @pytest.mark.parametrize("fhw", [(f, h, w) for f in (1, 5, 17, 33, 65, 129, 257)
                                  for h, w in ((256, 256), (544, 960), (720, 1280), (1104, 832), (16, 16), (960, 960))])
 def test_token_grid_matches_oracle(fhw):

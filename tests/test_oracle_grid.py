@@ -58,3 +58,21 @@ def test_patch_grid_halves_latent():
     for f, h, w in ((1, 256, 256), (33, 720, 1280), (5, 48, 80)):
         g = token_grid(f, h, w)
         assert g.gh * 2 == g.h_lat and g.gw * 2 == g.w_lat and g.gt == g.t_lat
+
+
+# Token counts of the other supported 129-frame sizes, worked by hand from the
+# grid the pages define (section 4 of the notes page: T' = (F-1)/4 + 1 = 33,
+# patch grid H/16 x W/16): 1104x832 -> 33*69*52, 624x832 -> 33*39*52,
+# 720x720 -> 33*45*45, 960x960 -> 33*60*60.
+HAND_WORKED = [
+    ((129, 1104, 832), (33, 69, 52), 118404),
+    ((129, 624, 832), (33, 39, 52), 66924),
+    ((129, 720, 720), (33, 45, 45), 66825),
+    ((129, 960, 960), (33, 60, 60), 118800),
+]
+
+
+@pytest.mark.parametrize("fhw,grid,n", HAND_WORKED, ids=lambda x: str(x))
+def test_hand_worked_token_counts(fhw, grid, n):
+    g = token_grid(*fhw)
+    assert (g.gt, g.gh, g.gw) == grid and g.n_video == n
