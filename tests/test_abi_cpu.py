@@ -1,6 +1,7 @@
 """C-ABI checks that need no GPU.
 
-* libhvattn.so loads and exports every function include/hvattn.h declares;
+* libhvattn.so loads and exports every function include/hvattn.h declares,
+  and imports no HIP allocation, copy, memset or synchronisation function;
 * hv_token_grid (host-only) agrees with the printed values and the oracle;
 * every host-side validation path of hv_rope3d_apply and
   hv_joint_attention_fwd returns its documented status without touching
@@ -42,6 +43,31 @@ def test_exports_every_declared_function():
     out = subprocess.run(["nm", "-D", "--defined-only", hv.library_path()], capture_output=True, text=True).stdout
     exported = sorted(set(re.findall(r" T (hv_[a-z0-9_]+)$", out, flags=re.M)))
     assert exported == names
+
+
+# The HIP runtime functions the library may import: kernel registration and
+# launch, the device query of the forward's CU count, the scratch address of
+# the allocation-free backward, and error reporting.  No allocation, no copy
+# or memset (which a caller's graph capture would record as separate nodes),
+# no synchronisation: the calls only enqueue kernels on the caller's stream.
+ALLOWED_HIP_IMPORTS = {
+    "__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+    "__hipRegisterFunction", "__hipRegisterVar", "__hipUnregisterFatBinary",
+    "hipLaunchKernel", "hipGetDevice", "hipDeviceGetAttribute", "hipGetSymbolAddress",
+    "hipGetLastError",
+}
+
+
+def test_library_imports_no_allocation_copy_or_synchronisation():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", hv.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    imported = {m.split("@")[0] for m in re.findall(r"\bU (\S+)", out)}
+    hip = {n for n in imported if "hip" in n.lower()}
+    assert hip, "no HIP imports found: nm output not understood"
+    assert hip <= ALLOWED_HIP_IMPORTS, sorted(hip - ALLOWED_HIP_IMPORTS)
+    banned = re.compile(r"malloc|free|memset|memcpy|synchron|hostregister", re.I)
+    assert not [n for n in hip if banned.search(n)]
 
 
 def test_status_strings():
