@@ -12,7 +12,9 @@ fp64 oracle, through the C ABI.
 * stress and edge cases: peaky softmax (Q x 8), identical keys (mean of V),
   theta = 256, NaN/huge values in padded K/V rows, determinism, every output
   row written (NaN-prefilled output), no writes outside the output rows
-  (guard rows around a strided view).
+  (guard rows around a strided view), q, k, v and out as views of fused
+  [B, L, 3, 24, 128] buffers (token stride of three head rows) giving the
+  bits of contiguous tensors, for both block sizes.
 """
 import numpy as np
 import pytest
@@ -172,6 +174,35 @@ def test_attention_deterministic_and_fully_written():
         outs.append(torch_to_bits(out))
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     assert np.all(np.isfinite(widen(outs[0])))
+
+
+@pytest.mark.parametrize("B,n_video,cap,valid", [
+    (1, 400, 50, [31]),          # 4-wave blocks, V in place
+    (2, 1300, 100, [100, 7]),    # 288 blocks of 256 rows: packed V, persistent workgroups
+])
+def test_attention_fused_qkv_views(B, n_video, cap, valid):
+    """q, k, v (and out) as views of fused [B, L, 3, 24, 128] buffers, so the
+    token stride is three head rows: the same bits as contiguous tensors."""
+    import torch
+    import rope_joint_attention_amd as hv
+
+    L = n_video + cap
+    bits = hvinputs.draw_qkv(B, L, seed=3 * L + B)
+    fused = torch.zeros((B, L, 3, 24, 128), dtype=torch.bfloat16, device="cuda")
+    for i, n in enumerate("qkv"):
+        fused[:, :, i] = bits_to_torch(bits[n])
+    out_f = torch.full((B, L, 3, 24, 128), 5.0, dtype=torch.bfloat16, device="cuda")
+    log(f"fused qkv views B={B} L={L} valid={valid}")
+    hv.hv_joint_attention_fwd(fused[:, :, 0], fused[:, :, 1], fused[:, :, 2], valid, n_video,
+                              out=out_f[:, :, 1])
+    flat = hv.hv_joint_attention_fwd(*(bits_to_torch(bits[n]) for n in "qkv"), valid, n_video)
+    torch.cuda.synchronize()
+    assert torch.all(out_f[:, :, 0] == 5.0) and torch.all(out_f[:, :, 2] == 5.0)
+    got = torch_to_bits(out_f[:, :, 1].contiguous())
+    assert np.array_equal(got, torch_to_bits(flat))
+    if B * L <= 1000:
+        ref = joint_attention(widen(bits["q"]), widen(bits["k"]), widen(bits["v"]), n_video, valid)
+        assert_close(widen(got), ref, "fused qkv views")
 
 
 def test_attention_guard_rows_untouched():
