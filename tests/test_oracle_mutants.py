@@ -77,6 +77,10 @@ MUTANTS = [
     ("chunked key gradients overwritten per chunk", "dk[bi, :lk, hi, :] += dkc", "dk[bi, :lk, hi, :] = dkc"),
     ("chunked dV uses dS", "return scale * (dp @ kb), scale * (dp.T @ qc), p.T @ gc",
      "return scale * (dp @ kb), scale * (dp.T @ qc), dp.T @ gc"),
+    ("chunked form drops a ragged last chunk", "starts = list(range(0, L, chunk))",
+     "starts = list(range(0, L - chunk + 1, chunk))"),
+    ("chunked dK drops the scale", "return scale * (dp @ kb), scale * (dp.T @ qc), p.T @ gc",
+     "return scale * (dp @ kb), (dp.T @ qc), p.T @ gc"),
     ("varlen backward key rows shifted", "kb, vb = k[k0:k1, h, :], v[k0:k1, h, :]",
      "kb, vb = k[k0:k1, h, :], v[q0:q0 + (k1 - k0), h, :]"),
 ]
