@@ -4,7 +4,8 @@ Each source under csrc/ is compiled for gfx950 (device code only, the
 library's flags) with -Rpass-analysis=kernel-resource-usage, and the report
 is checked against the budget the kernels are designed for: no scratch
 memory at all (no VGPR spills, no stack), the attention kernels at their
-occupancy (two waves per SIMD for the forward and dQ kernels, one for dK/dV),
+occupancy (two waves per SIMD for the 8-wave forward and the dQ kernel, one
+for the 4-wave forward of small calls and for dK/dV),
 and at most a bounded number of SGPRs spilled (those go to VGPR lanes, never
 to memory).  A change that starts spilling inside the key loop shows up here
 before it shows up as a slower kernel.
